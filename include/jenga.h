@@ -1,0 +1,183 @@
+/*
+ * jenga.h — C ABI of the MI355X (gfx950) token-sparse attention hot path of Jenga's
+ * contextual token sparsity.
+ *
+ * Citations name the pages the operations are defined on:
+ *   [summary] "JENGA: Enhancing LLM Long-Context Fine-tuning with Contextual Token Sparsity",
+ *             the aipaper.cc structured summary of the ATC'25 paper;
+ *   [notes]   the papercache.org deep-notes page of the same title.
+ *
+ * Conventions shared by every call
+ *   - Tensors are BSHD: [batch][token][head][head_dim] with head_dim contiguous.  q, k, v may
+ *     be strided views (strides in elements for batch, token and head); every other tensor
+ *     is dense as stated at its argument.
+ *   - All pointers are device pointers unless stated otherwise; the caller owns and frees
+ *     every buffer, including the workspace.  The library allocates nothing and keeps no
+ *     state between calls, so calls on different streams may run concurrently as long as
+ *     they do not share output buffers.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues work and
+ *     returns; there is no host synchronisation.  The kept-block count stays on the device.
+ *   - Errors: every argument check happens before anything is launched; a negative status
+ *     means nothing was enqueued.  JENGA_ERR_LAUNCH reports a failed launch (from
+ *     hipGetLastError).  Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Supported shapes: head_dim in {64, 128}; block a multiple of 64 (at most 1024) that
+ *     divides seq_len; n_heads_q a multiple of n_heads_kv; q/k/v rows 16-byte aligned.
+ */
+#ifndef JENGA_H
+#define JENGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { JENGA_DTYPE_F32 = 0, JENGA_DTYPE_BF16 = 1 } jenga_dtype;
+
+typedef enum {
+  JENGA_OK = 0,
+  JENGA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive size, bad stride or alignment */
+  JENGA_ERR_UNSUPPORTED = -2,  /* valid but unsupported shape (head_dim, block, dtype)      */
+  JENGA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than jenga_workspace_bytes   */
+  JENGA_ERR_LAUNCH = -4        /* a kernel launch failed                                    */
+} jenga_status;
+
+typedef enum {
+  JENGA_SELECT_TOPK = 0,        /* param = keep ratio r: keep jenga_topk_count(r, nKB) blocks  */
+  JENGA_SELECT_THRESH_REL = 1,  /* param = alpha: keep blocks with score >= alpha * mean score */
+  JENGA_SELECT_THRESH_ABS = 2   /* param = absolute per-layer threshold T                      */
+} jenga_select_mode;
+
+#define JENGA_FORCE_FIRST_BLOCK 1u  /* flag: block 0 is always kept */
+
+typedef enum { JENGA_OP_SCORE = 0, JENGA_OP_FWD = 1, JENGA_OP_BWD = 2 } jenga_op;
+
+/* Problem shape, shared by every call of one layer. */
+typedef struct jenga_problem {
+  int32_t batch;
+  int32_t seq_len;      /* S, tokens per sequence                                       */
+  int32_t n_heads_q;    /* Hq                                                           */
+  int32_t n_heads_kv;   /* Hkv (grouped-query attention when Hkv < Hq)                  */
+  int32_t head_dim;     /* D                                                            */
+  int32_t block;        /* b, tokens per token block (the unit of elimination)          */
+  int32_t dtype;        /* jenga_dtype of q, k, v and o_saved (MFMA operand type)       */
+  float scale;          /* softmax scale; 0 selects 1/sqrt(head_dim)                    */
+  int64_t q_stride[3];  /* batch, token, head strides of q, in elements                 */
+  int64_t k_stride[3];  /* batch, token, head strides of k, in elements                 */
+  int64_t v_stride[3];  /* batch, token, head strides of v, in elements                 */
+} jenga_problem;
+
+/* Status code -> static English string. */
+const char* jenga_status_string(int status);
+
+/* Number of blocks kept by top-k selection: ceil(r * n_blocks - 1e-6) clamped to
+ * [1, n_blocks] (r widened to double).  Host-side; returns -1 if n_blocks < 1. */
+int jenga_topk_count(float keep_ratio, int n_blocks);
+
+/* Workspace bytes needed by `op` (JENGA_OP_SCORE, _FWD or _BWD) for this problem.
+ * max_kept_blocks and n_segments only matter for JENGA_OP_BWD.  Returns 0 for an
+ * invalid problem (and for ops that need no workspace). */
+size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks, int n_segments);
+
+/*
+ * jenga_score_blocks — block-level token informativeness ([summary] 4.2.1 Eq. 1;
+ * 4.2.2 Eq. 2 head averaging; 4.2.3 aggregation of score blocks per key block).
+ *
+ * For every batch row and key block n:
+ *   block_scores[b][n] = (1/Hq) * sum_h sum_{j in block n} sum_{i > j} P^h_ij,
+ * where P^h is the causal softmax of scale * q_i . k_j over all S tokens of head h (KV head
+ * h / (Hq/Hkv)); the self term i = j is excluded as in Eq. 1.  Computed in two streamed
+ * passes (row log-sum-exp, then received mass per key) without storing any S x S matrix.
+ * The result is deterministic: per-key sums are fp64 and reduced in a fixed order.
+ *
+ *   q            [B][S][Hq][D] (dtype, strided per q_stride)
+ *   k            [B][S][Hkv][D] (dtype, strided per k_stride)
+ *   block_scores [B][S/block] fp32, dense, written
+ *   workspace    >= jenga_workspace_bytes(p, JENGA_OP_SCORE, 0, 1) bytes, 256-byte aligned
+ */
+int jenga_score_blocks(const jenga_problem* p, const void* q, const void* k, float* block_scores,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * jenga_select_blocks — token-block elimination against a per-layer threshold or a keep
+ * ratio ([notes] 4.2 layer-specific threshold; [summary] 4.2.3 Algorithm 1, step 1 sets the
+ * threshold from the average token-block score).
+ *
+ *   TOPK:       keep the jenga_topk_count(param, nKB) best blocks, ordered by score
+ *               descending then index ascending; NaN scores sort last.
+ *   THRESH_REL: T = (double)param * mean, the mean summed left to right in double;
+ *               keep blocks with (double)score >= T.
+ *   THRESH_ABS: the same with T = (double)param.
+ *   flags & JENGA_FORCE_FIRST_BLOCK: block 0 is kept (top-k then keeps block 0 plus the
+ *               best count-1 of the others).
+ *
+ *   block_scores [B][S/block] fp32, dense, read
+ *   kept_idx     [B][S/block] int32, dense, written: kept block indices ascending in the
+ *                first n_kept[b] entries; the rest is set to -1
+ *   n_kept       [B] int32, written (device memory)
+ * Only p->batch, p->seq_len and p->block are used.  Selection is exact and deterministic.
+ */
+int jenga_select_blocks(const jenga_problem* p, const float* block_scores, int mode, float param,
+                        unsigned flags, int32_t* kept_idx, int32_t* n_kept, void* stream);
+
+/*
+ * jenga_sparse_attn_fwd — permutation-free token-sparse causal attention forward
+ * ([notes] 4.4: kept tokens are loaded straight from the original tensors through the
+ * index list, and the attention output is added to the original input in place, which
+ * pads and residual-adds in one step; [summary] 3.1 attention formula).
+ *
+ * With T_k the tokens of the kept blocks of batch row b (kept rank r = position of the token
+ * among kept tokens in ascending order):
+ *   O_i = softmax_{j in T_k, j <= i}(scale * q_i . k_j) v_j   for i in T_k
+ *   resid[b][i][h][:] += O_i                                   for i in T_k
+ * Rows of eliminated tokens are never read as queries or keys and resid there is not
+ * written (bitwise unchanged).
+ *
+ *   kept_idx, n_kept   output of jenga_select_blocks (device)
+ *   max_kept_blocks    host upper bound on n_kept[b] (1 <= .. <= S/block); sizes the grids
+ *                      and the compact outputs; kept blocks beyond it are ignored
+ *   resid              [B][S][Hq][D] fp32, dense, read-modify-write
+ *   o_saved            [B][max_kept_blocks*block][Hq][D] dtype, dense, written by kept rank
+ *                      (the saved attention output used by the backward)
+ *   lse                [B][Hq][max_kept_blocks*block] fp32, dense, written by kept rank:
+ *                      natural-log softmax normaliser of each kept query
+ */
+int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, const void* v,
+                          const int32_t* kept_idx, const int32_t* n_kept, int max_kept_blocks,
+                          float* resid, void* o_saved, float* lse, void* stream);
+
+/*
+ * jenga_sparse_attn_bwd_segmented — backward of jenga_sparse_attn_fwd, computed over
+ * n_segments contiguous ranges of kept query ranks one after the other so that the
+ * transient buffers (the per-query dot(dO, O) terms and the operand copy of dOut) scale
+ * with the segment, not the sequence ([notes] 4.4 segment-based peak cutting: process
+ * segments independently, aggregate their gradients, discard each segment's activations).
+ *
+ * With P the forward's probabilities and dO_i = dout[b][i][h] for i in T_k:
+ *   D_i = dO_i . O_i;  dS_ij = P_ij (dO_i . v_j - D_i)
+ *   dq_i += scale sum_j dS_ij k_j;  dk_j += scale sum_{h in group} sum_i dS_ij q_i;
+ *   dv_j += sum_{h in group} sum_i P_ij dO_i
+ * The gradient through resid is the identity (dout itself) and needs no call.  The result
+ * does not depend on n_segments beyond fp32 rounding.
+ *
+ *   o_saved, lse      outputs of jenga_sparse_attn_fwd for the same inputs and kept set
+ *   dout              [B][S][Hq][D] fp32, dense, read at kept rows only
+ *   dq                [B][S][Hq][D] fp32, dense, accumulated (+=) at kept rows only
+ *   dk, dv            [B][S][Hkv][D] fp32, dense, accumulated (+=) at kept rows only
+ *   n_segments        1 <= n_segments <= max_kept_blocks*block/64
+ *   workspace         >= jenga_workspace_bytes(p, JENGA_OP_BWD, max_kept_blocks, n_segments)
+ * dq receives fp32 atomic additions, so its low bits may differ run to run.
+ */
+int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const void* k,
+                                    const void* v, const int32_t* kept_idx, const int32_t* n_kept,
+                                    int max_kept_blocks, const void* o_saved, const float* lse,
+                                    const float* dout, float* dq, float* dk, float* dv,
+                                    int n_segments, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JENGA_H */

@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+that include/jenga.h declares, and rejects bad arguments with the documented status before
+any launch.  Also pins the host-side top-k count against the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def J():
+    import token_sparse_attention_jenga_amd as J
+    return J
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "jenga.h")).read()
+    return sorted(set(re.findall(r"\b(jenga_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(J):
+    names = _declared_functions()
+    assert set(names) == set(J.EXPORTED), names
+    for n in names:
+        assert hasattr(J.lib, n), n
+        getattr(J.lib, n)                 # resolves the symbol
+
+
+def test_status_strings(J):
+    for st in (0, -1, -2, -3, -4):
+        assert J.status_string(st) != "unknown status"
+    assert J.status_string(7) == "unknown status"
+
+
+@pytest.mark.parametrize("r,n", [(0.5, 16), (0.35, 256), (0.5, 256), (0.3, 10), (0.31, 10), (1.0, 5),
+                                 (1e-9, 9), (0.25, 4), (0.999, 1000), (0.123, 4096)])
+def test_topk_count_matches_oracle(J, r, n):
+    assert J.topk_count(r, n) == oracle.keep_count(r, n)
+
+
+def _problem(J, B=1, S=1024, Hq=8, Hkv=8, D=64, block=64, dtype=0, scale=0.0):
+    p = J.JengaProblem()
+    p.batch, p.seq_len, p.n_heads_q, p.n_heads_kv, p.head_dim, p.block = B, S, Hq, Hkv, D, block
+    p.dtype, p.scale = dtype, scale
+    for name, H in (("q_stride", Hq), ("k_stride", Hkv), ("v_stride", Hkv)):
+        arr = getattr(p, name)
+        arr[0], arr[1], arr[2] = S * H * D, H * D, D
+    return p
+
+
+FAKE = 0x10000  # a 64 KiB-aligned non-null address; never dereferenced (checks fail first)
+
+
+def _score(J, p, ws_bytes=1 << 30, q=FAKE, ws=FAKE):
+    return J.lib.jenga_score_blocks(ctypes.byref(p), q, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_score_validation(J):
+    assert J.lib.jenga_score_blocks(None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == J.JENGA_ERR_INVALID_ARG
+    assert _score(J, _problem(J, D=96)) == J.JENGA_ERR_UNSUPPORTED
+    assert _score(J, _problem(J, D=128, dtype=0)) == J.JENGA_ERR_UNSUPPORTED     # fp32 needs D=64
+    assert _score(J, _problem(J, block=32)) == J.JENGA_ERR_UNSUPPORTED
+    assert _score(J, _problem(J, S=1000)) == J.JENGA_ERR_UNSUPPORTED
+    assert _score(J, _problem(J, Hq=6, Hkv=4)) == J.JENGA_ERR_INVALID_ARG
+    assert _score(J, _problem(J, dtype=5)) == J.JENGA_ERR_UNSUPPORTED
+    assert _score(J, _problem(J, B=0)) == J.JENGA_ERR_INVALID_ARG
+    assert _score(J, _problem(J, scale=-1.0)) == J.JENGA_ERR_INVALID_ARG
+    assert _score(J, _problem(J), q=0) == J.JENGA_ERR_INVALID_ARG
+    assert _score(J, _problem(J), q=FAKE + 4) == J.JENGA_ERR_INVALID_ARG           # misaligned
+    p = _problem(J)
+    need = J.workspace_bytes(p, J.JENGA_OP_SCORE)
+    assert need > 0
+    assert _score(J, p, ws_bytes=need - 1) == J.JENGA_ERR_WORKSPACE
+    assert _score(J, p, ws=0) == J.JENGA_ERR_WORKSPACE
+    bad = _problem(J)
+    bad.q_stride[1] = 8 * 64 + 2                                                     # row not 16-B aligned
+    assert _score(J, bad) == J.JENGA_ERR_INVALID_ARG
+
+
+def test_select_validation(J):
+    p = _problem(J)
+    f = lambda mode=0, param=0.5, flags=0, s=FAKE: J.lib.jenga_select_blocks(
+        ctypes.byref(p), s, mode, ctypes.c_float(param), flags, FAKE, FAKE, None)
+    assert f(mode=3) == J.JENGA_ERR_INVALID_ARG
+    assert f(param=0.0) == J.JENGA_ERR_INVALID_ARG
+    assert f(param=float("nan")) == J.JENGA_ERR_INVALID_ARG
+    assert f(flags=2) == J.JENGA_ERR_INVALID_ARG
+    assert f(s=0) == J.JENGA_ERR_INVALID_ARG
+    big = _problem(J, S=64 * 20000)
+    assert J.lib.jenga_select_blocks(ctypes.byref(big), FAKE, 0, ctypes.c_float(0.5), 0, FAKE, FAKE,
+                                     None) == J.JENGA_ERR_UNSUPPORTED
+
+
+def test_fwd_bwd_validation(J):
+    p = _problem(J)
+    fwd = lambda maxk=8, resid=FAKE: J.lib.jenga_sparse_attn_fwd(
+        ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, maxk, resid, FAKE, FAKE, None)
+    assert fwd(maxk=0) == J.JENGA_ERR_INVALID_ARG
+    assert fwd(maxk=17) == J.JENGA_ERR_INVALID_ARG
+    assert fwd(resid=0) == J.JENGA_ERR_INVALID_ARG
+    assert fwd(resid=FAKE + 8) == J.JENGA_ERR_INVALID_ARG
+    need = J.workspace_bytes(p, J.JENGA_OP_BWD, 8, 2)
+    assert need > 0
+    bwd = lambda nseg=2, ws_bytes=need, maxk=8: J.lib.jenga_sparse_attn_bwd_segmented(
+        ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, maxk, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        nseg, FAKE, ws_bytes, None)
+    assert bwd(nseg=0) == J.JENGA_ERR_INVALID_ARG
+    assert bwd(nseg=9) == J.JENGA_ERR_INVALID_ARG            # more segments than 64-row tiles
+    assert bwd(ws_bytes=need - 1) == J.JENGA_ERR_WORKSPACE
+    assert bwd(maxk=20) == J.JENGA_ERR_INVALID_ARG
+
+
+def test_workspace_scales_with_segments_and_kept_blocks(J):
+    p = _problem(J, S=32768, Hq=32, Hkv=32, D=128, block=128, dtype=1)
+    w1 = J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 1)
+    w8 = J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 8)
+    w8_half = J.workspace_bytes(p, J.JENGA_OP_BWD, 64, 8)
+    assert w8 * 7 < w1 <= w8 * 8 + 4096
+    assert abs(w8_half * 2 - w8) <= 4096
+    assert J.workspace_bytes(p, J.JENGA_OP_FWD) == 0

@@ -1,0 +1,201 @@
+"""GPU parity of each entry point against the oracle at sizes the oracle finishes in seconds.
+
+Shapes span several tiles and a ragged tail (odd kept-block counts against 128-row tiles),
+both operand dtypes, head_dim 64 and 128, block 64 and 128, grouped-query attention,
+scattered and empty kept sets, and 1 vs several backward segments.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (kept_tensor, max_abs, random_inputs, say, to_device, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def J():
+    import torch
+    assert torch.cuda.is_available()
+    import token_sparse_attention_jenga_amd as J
+    return J
+
+
+# ----------------------------------------------------------------------------------------
+# selection: bit-exact
+# ----------------------------------------------------------------------------------------
+
+def _select_cases():
+    rng = np.random.default_rng(123)
+    levels = np.float32([0.0, -0.0, 0.5, 1.0, 1.0, 2.0, np.nan, -3.0])
+    cases = []
+    for t in range(40):
+        n = int(rng.integers(1, 700))
+        if t % 3 == 0:
+            x = rng.choice(levels, n).astype(np.float32)
+        else:
+            x = rng.standard_normal(n).astype(np.float32)
+        mode = t % 3
+        param = [float(rng.uniform(0.05, 1.0)), float(rng.uniform(0.2, 2.0)),
+                 float(rng.standard_normal())][mode]
+        cases.append((x, mode, param, bool(t % 2)))
+    return cases
+
+
+def test_select_bit_exact(J):
+    import torch
+    for i, (x, mode, param, ff) in enumerate(_select_cases()):
+        say(f"select case {i} n={len(x)} mode={mode} param={param:.4f} force={ff}")
+        n = len(x)
+        S = n * 64
+        scores = torch.from_numpy(x[None].copy()).cuda()
+        kept, nk = J.select_blocks(scores, 64, S, mode, param, ff)
+        torch.cuda.synchronize()
+        ref = oracle.select_blocks(x, mode, param, ff)
+        got_n = int(nk.cpu()[0])
+        got = kept.cpu().numpy()[0]
+        assert got_n == len(ref), (i, got_n, len(ref))
+        assert np.array_equal(got[:got_n], ref), i
+        assert np.all(got[got_n:] == -1)
+
+
+def test_select_batched(J):
+    import torch
+    rng = np.random.default_rng(5)
+    x = rng.choice(np.float32([0.1, 0.2, 0.3]), (3, 256)).astype(np.float32)
+    say("select batched B=3 nkb=256")
+    kept, nk = J.select_blocks(torch.from_numpy(x).cuda(), 128, 256 * 128, J.JENGA_SELECT_TOPK, 0.35,
+                               True)
+    torch.cuda.synchronize()
+    for b in range(3):
+        ref = oracle.select_blocks(x[b], oracle.SELECT_TOPK, 0.35, True)
+        assert int(nk[b]) == len(ref) == 90
+        assert np.array_equal(kept.cpu().numpy()[b, :90], ref)
+
+
+# ----------------------------------------------------------------------------------------
+# scores: relative 1e-5
+# ----------------------------------------------------------------------------------------
+
+SCORE_CASES = [
+    # B, S, Hq, Hkv, D, block, dtype
+    (1, 1024, 8, 8, 64, 64, "f32"),
+    (1, 512, 4, 4, 128, 64, "bf16"),
+    (2, 384, 4, 2, 128, 128, "bf16"),
+    (1, 448, 2, 1, 64, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,block,dtype", SCORE_CASES)
+def test_scores(J, B, S, Hq, Hkv, D, block, dtype):
+    import torch
+    q, k, _, _, _ = random_inputs(B, S, Hq, Hkv, D, dtype, seed=S + Hq)
+    say(f"scores B{B} S{S} Hq{Hq} Hkv{Hkv} D{D} block{block} {dtype}")
+    got = J.score_blocks(to_device(q, dtype), to_device(k, dtype), block)
+    torch.cuda.synchronize()
+    ref = oracle.block_scores(q, k, block)
+    got = got.cpu().numpy().astype(np.float64)
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    assert rel <= 1e-5, rel
+
+
+def test_scores_head_subset_view(J):
+    """Strided head-subset views (the full-size score check uses them) match contiguous."""
+    import torch
+    B, S, Hq, Hkv, D, block = 1, 512, 8, 2, 128, 64
+    q, k, _, _, _ = random_inputs(B, S, Hq, Hkv, D, "bf16", seed=77)
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    say("scores head-subset view")
+    got = J.score_blocks(qd[:, :, 4:8], kd[:, :, 1:2], block)
+    torch.cuda.synchronize()
+    ref = oracle.block_scores(q[:, :, 4:8], k[:, :, 1:2], block)
+    assert np.max(np.abs(got.cpu().numpy() - ref) / ref) <= 1e-5
+
+
+# ----------------------------------------------------------------------------------------
+# forward / backward
+# ----------------------------------------------------------------------------------------
+
+ATTN_CASES = [
+    # B, S, Hq, Hkv, D, block, dtype, kept per batch, n_segments
+    (1, 1024, 8, 8, 64, 64, "f32", [[0, 1, 3, 4, 6, 9, 10, 15]], 3),
+    (1, 1024, 4, 4, 128, 64, "bf16", [[0, 2, 3, 5, 8, 9, 11, 12, 13]], 2),      # 9 blocks: ragged
+    (2, 1024, 4, 2, 128, 128, "bf16", [[1, 2, 4, 7], [0, 3, 5, 6]], 3),        # GQA, per-batch sets
+    (1, 768, 4, 1, 64, 64, "bf16", [list(range(12))], 4),                        # keep all, G=4
+    (1, 512, 2, 2, 128, 64, "bf16", [[7]], 1),                                   # one block
+    (1, 512, 2, 2, 64, 128, "f32", [[1, 3]], 2),
+]
+
+
+def _run_attn(J, q, k, v, x0, dout, kept_list, block, dtype, n_segments, maxk=None):
+    import torch
+    B, S = q.shape[0], q.shape[1]
+    nkb = S // block
+    maxk = max(max(len(x) for x in kept_list), 1) if maxk is None else maxk
+    qd, kd, vd = to_device(q, dtype), to_device(k, dtype), to_device(v, dtype)
+    kept_d, nk_d = kept_tensor(kept_list, nkb)
+    resid = torch.from_numpy(x0.copy()).cuda()
+    o_saved, lse = J.sparse_attn_fwd(qd, kd, vd, kept_d, nk_d, maxk, block, resid)
+    dq, dk, dv = J.sparse_attn_bwd(qd, kd, vd, kept_d, nk_d, maxk, block, o_saved, lse,
+                                   torch.from_numpy(dout).cuda(), n_segments)
+    torch.cuda.synchronize()
+    return (resid.cpu().numpy(), o_saved.float().cpu().numpy(), lse.cpu().numpy(),
+            dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,block,dtype,kept,nseg", ATTN_CASES)
+def test_fwd_bwd(J, B, S, Hq, Hkv, D, block, dtype, kept, nseg):
+    q, k, v, x0, dout = random_inputs(B, S, Hq, Hkv, D, dtype, seed=S + D + len(kept[0]))
+    say(f"fwd/bwd B{B} S{S} Hq{Hq} Hkv{Hkv} D{D} block{block} {dtype} kept={kept} N={nseg}")
+    resid, o_saved, lse, dq, dk, dv = _run_attn(J, q, k, v, x0, dout, kept, block, dtype, nseg)
+    tol = tol_for(dtype)
+    kept_np = [np.array(x) for x in kept]
+    O, LSE = oracle.attn_fwd(q, k, v, kept_np, block)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, kept_np, block, dout)
+    for b in range(B):
+        pos = oracle.token_positions(kept_np[b], block)
+        elim = np.setdiff1d(np.arange(S), pos)
+        assert np.array_equal(resid[b, elim], x0[b, elim])               # bitwise untouched
+        assert max_abs(resid[b, pos] - x0[b, pos], O[b, pos]) <= tol
+        assert max_abs(o_saved[b, :len(pos)], O[b, pos]) <= tol
+        lr = lse[b][:, :len(pos)]
+        assert np.max(np.abs(lr - LSE[b][:, pos]) / np.maximum(1.0, np.abs(LSE[b][:, pos]))) <= 1e-5
+        for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            err = max_abs(got[b, pos], ref[b, pos])
+            assert err <= tol, (name, err)
+            assert np.all(got[b, elim] == 0), name
+
+
+def test_bwd_segments_equivalent(J):
+    """N = 1 and N = 8 segments give the same gradients up to fp32 rounding."""
+    B, S, Hq, Hkv, D, block, dtype = 1, 2048, 4, 4, 128, 128, "bf16"
+    kept = [[0, 1, 2, 4, 5, 7, 8, 9, 11, 12, 15]]
+    q, k, v, x0, dout = random_inputs(B, S, Hq, Hkv, D, dtype, seed=3)
+    say("segments N=1 vs N=8")
+    r1 = _run_attn(J, q, k, v, x0, dout, kept, block, dtype, 1)
+    r8 = _run_attn(J, q, k, v, x0, dout, kept, block, dtype, 8)
+    for a, b in zip(r1[3:], r8[3:]):
+        scale = max(1.0, float(np.max(np.abs(a))))
+        assert max_abs(a, b) <= 1e-5 * scale
+
+
+def test_empty_kept_set_is_noop(J):
+    import torch
+    B, S, Hq, Hkv, D, block, dtype = 1, 512, 2, 2, 128, 64, "bf16"
+    q, k, v, x0, dout = random_inputs(B, S, Hq, Hkv, D, dtype, seed=9)
+    say("empty kept set")
+    resid, _, _, dq, dk, dv = _run_attn(J, q, k, v, x0, dout, [[]], block, dtype, 2, maxk=4)
+    assert np.array_equal(resid, x0)
+    assert not dq.any() and not dk.any() and not dv.any()
+
+
+def test_fwd_deterministic(J):
+    B, S, Hq, Hkv, D, block, dtype = 1, 1024, 4, 4, 128, 64, "bf16"
+    q, k, v, x0, dout = random_inputs(B, S, Hq, Hkv, D, dtype, seed=10)
+    kept = [[0, 2, 4, 6, 8, 10, 12, 14]]
+    say("determinism")
+    a = _run_attn(J, q, k, v, x0, dout, kept, block, dtype, 1)
+    b = _run_attn(J, q, k, v, x0, dout, kept, block, dtype, 1)
+    for x, y in zip(a[:3], b[:3]):
+        assert np.array_equal(x, y)
+    assert np.array_equal(a[4], b[4]) and np.array_equal(a[5], b[5])   # dk, dv: no atomics

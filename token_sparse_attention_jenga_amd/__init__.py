@@ -1,0 +1,227 @@
+"""Python binding of libjenga.so, the gfx950 token-sparse attention hot path.
+
+Argument marshalling only: every step runs in the library's HIP kernels.  PyTorch supplies
+device memory and the current stream.  Importing this package loads the library and fails
+loudly if it has not been built (python -m token_sparse_attention_jenga_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libjenga.so")
+
+JENGA_OK = 0
+JENGA_ERR_INVALID_ARG = -1
+JENGA_ERR_UNSUPPORTED = -2
+JENGA_ERR_WORKSPACE = -3
+JENGA_ERR_LAUNCH = -4
+JENGA_DTYPE_F32 = 0
+JENGA_DTYPE_BF16 = 1
+JENGA_SELECT_TOPK = 0
+JENGA_SELECT_THRESH_REL = 1
+JENGA_SELECT_THRESH_ABS = 2
+JENGA_FORCE_FIRST_BLOCK = 1
+JENGA_OP_SCORE = 0
+JENGA_OP_FWD = 1
+JENGA_OP_BWD = 2
+
+EXPORTED = ["jenga_status_string", "jenga_topk_count", "jenga_workspace_bytes",
+            "jenga_score_blocks", "jenga_select_blocks", "jenga_sparse_attn_fwd",
+            "jenga_sparse_attn_bwd_segmented"]
+
+
+class JengaProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("n_heads_q", ctypes.c_int32), ("n_heads_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+                ("v_stride", ctypes.c_int64 * 3)]
+
+
+class JengaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          f"`python -m token_sparse_attention_jenga_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    P = ctypes.POINTER(JengaProblem)
+    lib.jenga_status_string.argtypes = [i32]
+    lib.jenga_status_string.restype = ctypes.c_char_p
+    lib.jenga_topk_count.argtypes = [ctypes.c_float, i32]
+    lib.jenga_topk_count.restype = i32
+    lib.jenga_workspace_bytes.argtypes = [P, i32, i32, i32]
+    lib.jenga_workspace_bytes.restype = sz
+    lib.jenga_score_blocks.argtypes = [P, vp, vp, vp, vp, sz, vp]
+    lib.jenga_score_blocks.restype = i32
+    lib.jenga_select_blocks.argtypes = [P, vp, i32, ctypes.c_float, ctypes.c_uint, vp, vp, vp]
+    lib.jenga_select_blocks.restype = i32
+    lib.jenga_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
+    lib.jenga_sparse_attn_fwd.restype = i32
+    lib.jenga_sparse_attn_bwd_segmented.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                                    vp, i32, vp, sz, vp]
+    lib.jenga_sparse_attn_bwd_segmented.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.jenga_status_string(int(status)).decode()
+
+
+def topk_count(keep_ratio: float, n_blocks: int) -> int:
+    return int(lib.jenga_topk_count(ctypes.c_float(keep_ratio), int(n_blocks)))
+
+
+# ------------------------------------------------------------------------------------------
+# torch-facing helpers (torch is imported lazily: the library itself needs no torch)
+# ------------------------------------------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return JENGA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return JENGA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_problem(q, k, v=None, block: int = 64, scale: float = 0.0) -> JengaProblem:
+    """Problem descriptor from BSHD tensors (views allowed: strides are passed through)."""
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    p = JengaProblem()
+    p.batch, p.seq_len, p.n_heads_q, p.n_heads_kv, p.head_dim, p.block = B, S, Hq, Hkv, D, block
+    p.dtype = _dtype_code(q)
+    p.scale = float(scale)
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v if v is not None else k)):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name}: head_dim must be contiguous")
+        arr = getattr(p, name)
+        arr[0], arr[1], arr[2] = t.stride(0), t.stride(1), t.stride(2)
+    return p
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(fn: str, st: int):
+    if st != JENGA_OK:
+        raise JengaError(fn, st)
+
+
+def workspace_bytes(p: JengaProblem, op: int, max_kept_blocks: int = 0, n_segments: int = 1) -> int:
+    return int(lib.jenga_workspace_bytes(ctypes.byref(p), op, max_kept_blocks, n_segments))
+
+
+def alloc_workspace(nbytes: int, device):
+    import torch
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def jenga_score_blocks(p: JengaProblem, q, k, block_scores, workspace, stream=None) -> None:
+    st = lib.jenga_score_blocks(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(block_scores),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _check("jenga_score_blocks", st)
+
+
+def jenga_select_blocks(p: JengaProblem, block_scores, mode: int, param: float, flags: int,
+                        kept_idx, n_kept, stream=None) -> None:
+    st = lib.jenga_select_blocks(ctypes.byref(p), _ptr(block_scores), int(mode),
+                                 ctypes.c_float(param), int(flags), _ptr(kept_idx), _ptr(n_kept),
+                                 _stream(stream))
+    _check("jenga_select_blocks", st)
+
+
+def jenga_sparse_attn_fwd(p: JengaProblem, q, k, v, kept_idx, n_kept, max_kept_blocks: int,
+                          resid, o_saved, lse, stream=None) -> None:
+    st = lib.jenga_sparse_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_idx),
+                                   _ptr(n_kept), int(max_kept_blocks), _ptr(resid), _ptr(o_saved),
+                                   _ptr(lse), _stream(stream))
+    _check("jenga_sparse_attn_fwd", st)
+
+
+def jenga_sparse_attn_bwd_segmented(p: JengaProblem, q, k, v, kept_idx, n_kept,
+                                    max_kept_blocks: int, o_saved, lse, dout, dq, dk, dv,
+                                    n_segments: int, workspace, stream=None) -> None:
+    st = lib.jenga_sparse_attn_bwd_segmented(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_idx), _ptr(n_kept),
+        int(max_kept_blocks), _ptr(o_saved), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        int(n_segments), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check("jenga_sparse_attn_bwd_segmented", st)
+
+
+# ------------------------------------------------------------------------------------------
+# Convenience layer: allocate outputs with torch and call the entry points above
+# ------------------------------------------------------------------------------------------
+
+def score_blocks(q, k, block: int, scale: float = 0.0):
+    import torch
+    p = make_problem(q, k, None, block, scale)
+    out = torch.empty((q.shape[0], q.shape[1] // block), dtype=torch.float32, device=q.device)
+    ws = alloc_workspace(workspace_bytes(p, JENGA_OP_SCORE), q.device)
+    jenga_score_blocks(p, q, k, out, ws)
+    return out
+
+
+def select_blocks(scores, block: int, seq_len: int, mode: int, param: float,
+                  force_first: bool = False) -> Tuple[object, object]:
+    import torch
+    B, nkb = scores.shape
+    p = JengaProblem()
+    p.batch, p.seq_len, p.block = B, seq_len, block
+    kept = torch.empty((B, nkb), dtype=torch.int32, device=scores.device)
+    n_kept = torch.empty((B,), dtype=torch.int32, device=scores.device)
+    jenga_select_blocks(p, scores, mode, param, JENGA_FORCE_FIRST_BLOCK if force_first else 0,
+                        kept, n_kept)
+    return kept, n_kept
+
+
+def sparse_attn_fwd(q, k, v, kept_idx, n_kept, max_kept_blocks: int, block: int, resid,
+                    scale: float = 0.0):
+    """resid is updated in place; returns (o_saved, lse) sized by max_kept_blocks."""
+    import torch
+    p = make_problem(q, k, v, block, scale)
+    B, S, Hq, D = q.shape
+    ncap = max_kept_blocks * block
+    o_saved = torch.empty((B, ncap, Hq, D), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, ncap), dtype=torch.float32, device=q.device)
+    jenga_sparse_attn_fwd(p, q, k, v, kept_idx, n_kept, max_kept_blocks, resid, o_saved, lse)
+    return o_saved, lse
+
+
+def sparse_attn_bwd(q, k, v, kept_idx, n_kept, max_kept_blocks: int, block: int, o_saved, lse,
+                    dout, n_segments: int = 1, scale: float = 0.0, grads=None):
+    """Returns (dq, dk, dv) fp32; accumulates into `grads` when given."""
+    import torch
+    p = make_problem(q, k, v, block, scale)
+    if grads is None:
+        dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+        dk = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
+        dv = torch.zeros(v.shape, dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv = grads
+    ws = alloc_workspace(workspace_bytes(p, JENGA_OP_BWD, max_kept_blocks, n_segments), q.device)
+    jenga_sparse_attn_bwd_segmented(p, q, k, v, kept_idx, n_kept, max_kept_blocks, o_saved, lse,
+                                    dout, dq, dk, dv, n_segments, ws)
+    return dq, dk, dv

@@ -1,0 +1,260 @@
+// C ABI of the token-sparse attention hot path: argument validation, workspace sizing,
+// launch geometry and the segment loop.  Every check happens before the first launch.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/jenga.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxBlocks = 16384;      // selection keeps one 32-bit key per block in LDS
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_problem(const jenga_problem* p, bool need_qkv_strides) {
+  if (!p) return JENGA_ERR_INVALID_ARG;
+  if (p->batch <= 0 || p->seq_len <= 0 || p->n_heads_q <= 0 || p->n_heads_kv <= 0 ||
+      p->head_dim <= 0 || p->block <= 0)
+    return JENGA_ERR_INVALID_ARG;
+  if (p->n_heads_q % p->n_heads_kv != 0) return JENGA_ERR_INVALID_ARG;
+  if (!(p->scale >= 0.f) || isinf(p->scale)) return JENGA_ERR_INVALID_ARG;
+  if (p->block % 64 != 0 || p->block > 1024) return JENGA_ERR_UNSUPPORTED;
+  if (p->seq_len % p->block != 0) return JENGA_ERR_UNSUPPORTED;
+  if (p->seq_len / p->block > kMaxBlocks) return JENGA_ERR_UNSUPPORTED;
+  if (p->dtype != JENGA_DTYPE_F32 && p->dtype != JENGA_DTYPE_BF16) return JENGA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return JENGA_ERR_UNSUPPORTED;
+  if (p->dtype == JENGA_DTYPE_F32 && p->head_dim != 64) return JENGA_ERR_UNSUPPORTED;
+  if (need_qkv_strides) {
+    const int es = p->dtype == JENGA_DTYPE_BF16 ? 2 : 4;
+    const int64_t* st[3] = {p->q_stride, p->k_stride, p->v_stride};
+    for (int t = 0; t < 3; ++t)
+      for (int i = 0; i < 3; ++i)
+        if (st[t][i] < 0 || (st[t][i] * es) % 16 != 0) return JENGA_ERR_INVALID_ARG;
+  }
+  return JENGA_OK;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+float scale_of(const jenga_problem* p) {
+  return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+}
+
+void copy_strides(int64_t dst[3], const int64_t src[3]) {
+  for (int i = 0; i < 3; ++i) dst[i] = src[i];
+}
+
+// Segment length in kept ranks: ceil(Nk_cap / N) rounded up to the 64-query tile.
+int seg_len_of(int ncap, int n_segments) {
+  int L = (ncap + n_segments - 1) / n_segments;
+  return (L + 63) / 64 * 64;
+}
+
+size_t bwd_ws_bytes(const jenga_problem* p, int max_kept_blocks, int n_segments) {
+  const int ncap = max_kept_blocks * p->block;
+  const int L = seg_len_of(ncap, n_segments);
+  const size_t es = p->dtype == JENGA_DTYPE_BF16 ? 2 : 4;
+  const size_t d_bytes = (size_t)p->batch * p->n_heads_q * L * sizeof(float);
+  const size_t do_bytes = (size_t)p->batch * L * p->n_heads_q * p->head_dim * es;
+  return align_up(d_bytes) + align_up(do_bytes);
+}
+
+size_t score_ws_bytes(const jenga_problem* p) {
+  const size_t lse = (size_t)p->batch * p->n_heads_q * p->seq_len * sizeof(float);
+  const size_t mass = (size_t)p->batch * p->n_heads_q * (p->seq_len / 32) * sizeof(double);
+  return align_up(lse) + align_up(mass);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* jenga_status_string(int status) {
+  switch (status) {
+    case JENGA_OK: return "ok";
+    case JENGA_ERR_INVALID_ARG: return "invalid argument";
+    case JENGA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case JENGA_ERR_WORKSPACE: return "workspace missing or too small";
+    case JENGA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int jenga_topk_count(float keep_ratio, int n_blocks) {
+  if (n_blocks < 1) return -1;
+  const double r = (double)keep_ratio;
+  if (!(r == r)) return 1;
+  double k = ceil(r * (double)n_blocks - 1e-6);
+  if (k < 1.0) k = 1.0;
+  if (k > (double)n_blocks) k = (double)n_blocks;
+  return (int)k;
+}
+
+size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks, int n_segments) {
+  if (check_problem(p, false) != JENGA_OK) return 0;
+  if (op == JENGA_OP_SCORE) return score_ws_bytes(p);
+  if (op == JENGA_OP_FWD) return 0;
+  if (op == JENGA_OP_BWD) {
+    const int nkb = p->seq_len / p->block;
+    if (max_kept_blocks < 1 || max_kept_blocks > nkb || n_segments < 1) return 0;
+    if (n_segments > max_kept_blocks * p->block / 64) return 0;
+    return bwd_ws_bytes(p, max_kept_blocks, n_segments);
+  }
+  return 0;
+}
+
+int jenga_score_blocks(const jenga_problem* p, const void* q, const void* k, float* block_scores,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_problem(p, true);
+  if (st != JENGA_OK) return st;
+  if (!q || !k || !block_scores) return JENGA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k)) return JENGA_ERR_INVALID_ARG;
+  const size_t need = score_ws_bytes(p);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+    return JENGA_ERR_WORKSPACE;
+  jenga::ScoreParams sp;
+  sp.q = q;
+  sp.k = k;
+  copy_strides(sp.qs, p->q_stride);
+  copy_strides(sp.ks, p->k_stride);
+  sp.B = p->batch;
+  sp.S = p->seq_len;
+  sp.Hq = p->n_heads_q;
+  sp.Hkv = p->n_heads_kv;
+  sp.block = p->block;
+  sp.scale_log2 = scale_of(p) * 1.4426950408889634f;
+  sp.lse2 = (float*)workspace;
+  sp.mass32 = (double*)((char*)workspace +
+                        align_up((size_t)p->batch * p->n_heads_q * p->seq_len * sizeof(float)));
+  sp.scores = block_scores;
+  if (jenga::launch_score(sp, p->dtype, p->head_dim, (hipStream_t)stream) != hipSuccess)
+    return JENGA_ERR_LAUNCH;
+  return JENGA_OK;
+}
+
+int jenga_select_blocks(const jenga_problem* p, const float* block_scores, int mode, float param,
+                        unsigned flags, int32_t* kept_idx, int32_t* n_kept, void* stream) {
+  if (!p) return JENGA_ERR_INVALID_ARG;
+  if (p->batch <= 0 || p->seq_len <= 0 || p->block <= 0) return JENGA_ERR_INVALID_ARG;
+  if (p->seq_len % p->block != 0) return JENGA_ERR_UNSUPPORTED;
+  const int nkb = p->seq_len / p->block;
+  if (nkb > kMaxBlocks) return JENGA_ERR_UNSUPPORTED;
+  if (!block_scores || !kept_idx || !n_kept) return JENGA_ERR_INVALID_ARG;
+  if (mode != JENGA_SELECT_TOPK && mode != JENGA_SELECT_THRESH_REL && mode != JENGA_SELECT_THRESH_ABS)
+    return JENGA_ERR_INVALID_ARG;
+  if ((flags & ~JENGA_FORCE_FIRST_BLOCK) != 0) return JENGA_ERR_INVALID_ARG;
+  if (mode == JENGA_SELECT_TOPK && !(param > 0.f)) return JENGA_ERR_INVALID_ARG;
+  jenga::SelectParams sp;
+  sp.scores = block_scores;
+  sp.B = p->batch;
+  sp.nkb = nkb;
+  sp.mode = mode;
+  sp.kcount = mode == JENGA_SELECT_TOPK ? jenga_topk_count(param, nkb) : 0;
+  sp.param = param;
+  sp.flags = flags;
+  sp.kept_idx = kept_idx;
+  sp.n_kept = n_kept;
+  if (jenga::launch_select(sp, (hipStream_t)stream) != hipSuccess) return JENGA_ERR_LAUNCH;
+  return JENGA_OK;
+}
+
+int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, const void* v,
+                          const int32_t* kept_idx, const int32_t* n_kept, int max_kept_blocks,
+                          float* resid, void* o_saved, float* lse, void* stream) {
+  int st = check_problem(p, true);
+  if (st != JENGA_OK) return st;
+  const int nkb = p->seq_len / p->block;
+  if (!q || !k || !v || !kept_idx || !n_kept || !resid || !o_saved || !lse)
+    return JENGA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(resid) || !aligned16(o_saved))
+    return JENGA_ERR_INVALID_ARG;
+  if (max_kept_blocks < 1 || max_kept_blocks > nkb) return JENGA_ERR_INVALID_ARG;
+  jenga::FwdParams fp;
+  fp.q = q;
+  fp.k = k;
+  fp.v = v;
+  copy_strides(fp.qs, p->q_stride);
+  copy_strides(fp.ks, p->k_stride);
+  copy_strides(fp.vs, p->v_stride);
+  fp.kept = kept_idx;
+  fp.n_kept = n_kept;
+  fp.resid = resid;
+  fp.o_saved = o_saved;
+  fp.lse = lse;
+  fp.B = p->batch;
+  fp.S = p->seq_len;
+  fp.Hq = p->n_heads_q;
+  fp.Hkv = p->n_heads_kv;
+  fp.block = p->block;
+  fp.nkb = nkb;
+  fp.max_kept_blocks = max_kept_blocks;
+  fp.ncap = max_kept_blocks * p->block;
+  fp.scale_log2 = scale_of(p) * 1.4426950408889634f;
+  if (jenga::launch_fwd(fp, p->dtype, p->head_dim, (hipStream_t)stream) != hipSuccess)
+    return JENGA_ERR_LAUNCH;
+  return JENGA_OK;
+}
+
+int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const void* k,
+                                    const void* v, const int32_t* kept_idx, const int32_t* n_kept,
+                                    int max_kept_blocks, const void* o_saved, const float* lse,
+                                    const float* dout, float* dq, float* dk, float* dv,
+                                    int n_segments, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  int st = check_problem(p, true);
+  if (st != JENGA_OK) return st;
+  const int nkb = p->seq_len / p->block;
+  if (!q || !k || !v || !kept_idx || !n_kept || !o_saved || !lse || !dout || !dq || !dk || !dv)
+    return JENGA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_saved) || !aligned16(dout))
+    return JENGA_ERR_INVALID_ARG;
+  if (max_kept_blocks < 1 || max_kept_blocks > nkb) return JENGA_ERR_INVALID_ARG;
+  const int ncap = max_kept_blocks * p->block;
+  if (n_segments < 1 || n_segments > ncap / 64) return JENGA_ERR_INVALID_ARG;
+  const size_t need = bwd_ws_bytes(p, max_kept_blocks, n_segments);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+    return JENGA_ERR_WORKSPACE;
+  const int L = seg_len_of(ncap, n_segments);
+  jenga::BwdParams bp;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  copy_strides(bp.qs, p->q_stride);
+  copy_strides(bp.ks, p->k_stride);
+  copy_strides(bp.vs, p->v_stride);
+  bp.kept = kept_idx;
+  bp.n_kept = n_kept;
+  bp.o_saved = o_saved;
+  bp.lse = lse;
+  bp.dout = dout;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.wsD = (float*)workspace;
+  bp.wsdO = (char*)workspace + align_up((size_t)p->batch * p->n_heads_q * L * sizeof(float));
+  bp.B = p->batch;
+  bp.S = p->seq_len;
+  bp.Hq = p->n_heads_q;
+  bp.Hkv = p->n_heads_kv;
+  bp.block = p->block;
+  bp.nkb = nkb;
+  bp.max_kept_blocks = max_kept_blocks;
+  bp.ncap = ncap;
+  bp.seg_len = L;
+  bp.scale = scale_of(p);
+  bp.scale_log2 = bp.scale * 1.4426950408889634f;
+  for (int s = 0; s < n_segments; ++s) {
+    if ((int64_t)s * L >= ncap) break;
+    bp.seg = s;
+    if (jenga::launch_bwd_segment(bp, p->dtype, p->head_dim, (hipStream_t)stream) != hipSuccess)
+      return JENGA_ERR_LAUNCH;
+  }
+  return JENGA_OK;
+}
+
+}  // extern "C"

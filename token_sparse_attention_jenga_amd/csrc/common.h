@@ -1,0 +1,116 @@
+// Shared device helpers for the gfx950 kernels: MFMA operand traits, LDS transpose reads,
+// bf16 conversion, and the kept-rank -> token-position map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+namespace jenga {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------------------
+// MFMA 32x32 traits.  For both operand types the accumulator layout is the same: lane l,
+// register r holds C[8*(r/4) + 4*(l/32) + r%4][l%32].  Operands: lane l supplies
+// A[l%32][KSTEP*s + KPL*(l/32) + i] and B[KSTEP*s + KPL*(l/32) + i][l%32], i < KPL.
+// ---------------------------------------------------------------------------------------
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16> {
+  using frag = bf16x8;
+  static constexpr int KPL = 8;
+  static constexpr int KSTEP = 16;
+  __device__ static inline f32x16 mma(const frag& a, const frag& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  using frag = float;
+  static constexpr int KPL = 1;
+  static constexpr int KSTEP = 2;
+  __device__ static inline f32x16 mma(const frag& a, const frag& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ inline f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Round-to-nearest-even float -> bf16 bits (inputs are finite).
+__device__ inline uint32_t bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight fp32 values -> one bf16x8 MFMA operand.
+__device__ inline bf16x8 to_frag8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                  float a6, float a7) {
+  u32x4 w;
+  w[0] = pack_bf16x2(a0, a1);
+  w[1] = pack_bf16x2(a2, a3);
+  w[2] = pack_bf16x2(a4, a5);
+  w[3] = pack_bf16x2(a6, a7);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// LDS transpose read of 16-bit data (gfx950).  Within every group of 16 lanes, lane j
+// receives element j%4 of the 8-byte words addressed by lanes 4*i + j/4, i = 0..3.  If lane s
+// of the group addresses row R + s/4, column C + 4*(s%4) of a row-major tile, lane j
+// therefore receives tile[R + i][C + j] for i = 0..3: four consecutive rows of one column.
+__device__ inline s16x4 lds_read_tr16(const LDS_AS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p);
+}
+
+// bf16 A/B operand whose reduction index runs down the rows of a row-major LDS tile:
+// lane l receives tile[row0(t) + s/4 ... ][col] for two instructions t = 0, 1, where the
+// caller supplies the first row of each 4-row run seen by this lane's half-wave.
+// col0: first column of the 32-wide operand block (elements).
+__device__ inline bf16x8 lds_frag_tr(const LDS_AS char* tile, int ld_bytes, int row_t0,
+                                     int row_t1, int col0) {
+  const int l = threadIdx.x & 63;
+  const int s = l & 15;
+  const int col = col0 + 16 * ((l >> 4) & 1) + 4 * (s & 3);
+  const LDS_AS char* p0 = tile + (row_t0 + (s >> 2)) * ld_bytes + col * 2;
+  const LDS_AS char* p1 = tile + (row_t1 + (s >> 2)) * ld_bytes + col * 2;
+  s16x4 a = lds_read_tr16(p0);
+  s16x4 b = lds_read_tr16(p1);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Token position of kept rank r (ranks are in ascending position order).
+__device__ inline int rank_to_pos(const int32_t* __restrict__ kept, int block, int r) {
+  const int kb = r / block;
+  return kept[kb] * block + (r - kb * block);
+}
+
+// 16-byte global load / store helpers.
+__device__ inline u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ inline void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+
+__device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+}  // namespace jenga

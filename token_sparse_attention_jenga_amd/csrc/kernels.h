@@ -1,0 +1,68 @@
+// Launch interface between the C ABI layer (api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jenga {
+
+struct ScoreParams {
+  const void* q;
+  const void* k;
+  int64_t qs[3], ks[3];
+  int B, S, Hq, Hkv, block;
+  float scale_log2;   // softmax scale * log2(e)
+  float* lse2;        // workspace [B][Hq][S]: log2-domain row normaliser
+  double* mass32;     // workspace [B][Hq][S/32]: received mass per 32-key group
+  float* scores;      // [B][S/block]
+};
+
+struct SelectParams {
+  const float* scores;
+  int B, nkb, mode, kcount;
+  float param;
+  unsigned flags;
+  int32_t* kept_idx;
+  int32_t* n_kept;
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t qs[3], ks[3], vs[3];
+  const int32_t* kept;
+  const int32_t* n_kept;
+  float* resid;
+  void* o_saved;
+  float* lse;
+  int B, S, Hq, Hkv, block, nkb, max_kept_blocks, ncap;
+  float scale_log2;
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t qs[3], ks[3], vs[3];
+  const int32_t* kept;
+  const int32_t* n_kept;
+  const void* o_saved;
+  const float* lse;
+  const float* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* wsD;    // [B][Hq][L]   dot(dO, O) of the segment's queries
+  void* wsdO;    // [B][L][Hq][D] dOut rows of the segment in operand dtype, by kept rank
+  int B, S, Hq, Hkv, block, nkb, max_kept_blocks, ncap, seg_len, seg;
+  float scale, scale_log2;
+};
+
+// dtype: 0 = fp32 operands, 1 = bf16 operands.  Each returns hipGetLastError().
+hipError_t launch_score(const ScoreParams& p, int dtype, int D, hipStream_t st);
+hipError_t launch_select(const SelectParams& p, hipStream_t st);
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, hipStream_t st);
+hipError_t launch_bwd_segment(const BwdParams& p, int dtype, int D, hipStream_t st);
+
+}  // namespace jenga
