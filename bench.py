@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the token-sparse attention hot path on one MI355X.
+
+One step = the whole path over one batch: for every layer, block scoring -> block selection
+-> permutation-free sparse attention forward (residual updated in place), then the segmented
+backward of every layer in reverse order.  Inputs are seeded synthetic tensors already
+resident in HBM.  Prints ONE JSON line.
+
+The metric counts kept-token FLOPs of the attention forward and backward only:
+fwd = 4*D*Hq*P and bwd = 10*D*Hq*P per batch row, P = Nk(Nk+1)/2 causal pairs among the
+Nk kept tokens; recomputation and scoring FLOPs are not counted.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 bf16 flop/clk/CU x 2.4 GHz, dense
+HBM_PEAK_GBS = 8000.0
+METRIC = "fwd+bwd token-sparse attn TFLOP/s (kept FLOPs) & tokens/s at S=32K; % MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="c5", help="workload name (c1..c5); c5 is the S=32K one")
+    ap.add_argument("--kept", choices=["selected", "scattered"], default="selected",
+                    help="attention over the selected blocks, or over a seeded scattered set")
+    ap.add_argument("--segments", type=int, default=0, help="override backward segment count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "token_sparse_attention_jenga_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the token-sparse attention path here is single-GPU "
+              "(no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import token_sparse_attention_jenga_amd as J
+    from synth import config_by_name
+    from synth.generate import make_layer, make_resid_dout, random_kept_blocks
+
+    cfg = config_by_name(args.config)
+    dev = torch.device("cuda:0")
+    B, S, Hq, Hkv, D, blk = cfg.batch, cfg.seq_len, cfg.n_heads_q, cfg.n_heads_kv, cfg.head_dim, cfg.block
+    nkb = S // blk
+    L = cfg.n_layers
+    nseg = args.segments or cfg.n_segments
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    # ---------------- inputs (seeded, generated on the host in parallel, then resident) ----
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(max_workers=min(L, 8)) as ex:
+        futs = [ex.submit(make_layer, cfg, l, None, False) for l in range(L)]
+        x0_np, dout_np = make_resid_dout(cfg)
+        layers_np = [f.result() for f in futs]
+    layers = []
+    for l, li in enumerate(layers_np):
+        q = torch.from_numpy(li.q).to(dev).to(tdt)       # RNE cast on the device: same bits as
+        k = torch.from_numpy(li.k).to(dev).to(tdt)       # the host-side rounding of the oracle
+        v = torch.from_numpy(li.v).to(dev).to(tdt)
+        layers.append({"q": q, "k": k, "v": v})
+    gen_s = time.time() - t0
+    x0 = torch.from_numpy(x0_np).to(dev)
+    dout = torch.from_numpy(dout_np).to(dev)
+    resid = x0.clone()
+    sample_np = (layers_np[0].q[:, :, :8], layers_np[0].k[:, :, :8], layers_np[0].v[:, :, :8],
+                 dout_np[:, :, :8])
+    del layers_np, x0_np
+
+    if cfg.select_mode == "topk":
+        mode, maxk = J.JENGA_SELECT_TOPK, J.topk_count(cfg.select_param, nkb)
+    else:
+        mode, maxk = J.JENGA_SELECT_THRESH_REL, nkb
+    flags = J.JENGA_FORCE_FIRST_BLOCK if cfg.force_first else 0
+    ncap = maxk * blk
+    for l, st in enumerate(layers):
+        p = J.make_problem(st["q"], st["k"], st["v"], blk)
+        st["p"] = p
+        st["scores"] = torch.empty((B, nkb), dtype=torch.float32, device=dev)
+        st["kept"] = torch.empty((B, nkb), dtype=torch.int32, device=dev)
+        st["nk"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        st["o"] = torch.empty((B, ncap, Hq, D), dtype=tdt, device=dev)
+        st["lse"] = torch.empty((B, Hq, ncap), dtype=torch.float32, device=dev)
+        st["dq"] = torch.zeros((B, S, Hq, D), dtype=torch.float32, device=dev)
+        st["dk"] = torch.zeros((B, S, Hkv, D), dtype=torch.float32, device=dev)
+        st["dv"] = torch.zeros((B, S, Hkv, D), dtype=torch.float32, device=dev)
+        st["ws_s"] = J.alloc_workspace(J.workspace_bytes(p, J.JENGA_OP_SCORE), dev)
+        st["ws_b"] = J.alloc_workspace(J.workspace_bytes(p, J.JENGA_OP_BWD, maxk, nseg), dev)
+        if args.kept == "scattered":
+            kb = random_kept_blocks(nkb, maxk, 5999 + l)
+            arr = np.full((B, nkb), -1, np.int32)
+            arr[:, :maxk] = kb
+            st["kept_att"] = torch.from_numpy(arr).to(dev)
+            st["nk_att"] = torch.full((B,), maxk, dtype=torch.int32, device=dev)
+
+    stream = torch.cuda.current_stream()
+
+    def run_step(ev=None):
+        for l, st in enumerate(layers):
+            if ev is not None:
+                ev[l][0].record(stream)
+            J.jenga_score_blocks(st["p"], st["q"], st["k"], st["scores"], st["ws_s"])
+            if ev is not None:
+                ev[l][1].record(stream)
+            J.jenga_select_blocks(st["p"], st["scores"], mode, cfg.select_param, flags, st["kept"], st["nk"])
+            if ev is not None:
+                ev[l][2].record(stream)
+            ka, na = (st["kept_att"], st["nk_att"]) if args.kept == "scattered" else (st["kept"], st["nk"])
+            J.jenga_sparse_attn_fwd(st["p"], st["q"], st["k"], st["v"], ka, na, maxk, resid, st["o"],
+                                    st["lse"])
+            if ev is not None:
+                ev[l][3].record(stream)
+        for l in reversed(range(L)):
+            st = layers[l]
+            ka, na = (st["kept_att"], st["nk_att"]) if args.kept == "scattered" else (st["kept"], st["nk"])
+            if ev is not None:
+                ev[l][4].record(stream)
+            J.jenga_sparse_attn_bwd_segmented(st["p"], st["q"], st["k"], st["v"], ka, na, maxk, st["o"],
+                                              st["lse"], dout, st["dq"], st["dk"], st["dv"], nseg,
+                                              st["ws_b"])
+            if ev is not None:
+                ev[l][5].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    nks = []
+    for st in layers:
+        na = st["nk_att"] if args.kept == "scattered" else st["nk"]
+        nks.append([int(x) * blk for x in na.cpu().numpy()])
+
+    K = args.steps
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        run_step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+    phase = {"score": 0.0, "select": 0.0, "fwd": 0.0, "bwd": 0.0}
+    for i in range(K):
+        for l in range(L):
+            e = evs[i][l]
+            phase["score"] += e[0].elapsed_time(e[1])
+            phase["select"] += e[1].elapsed_time(e[2])
+            phase["fwd"] += e[2].elapsed_time(e[3])
+            phase["bwd"] += e[4].elapsed_time(e[5])
+    phase = {kk: vv / K for kk, vv in phase.items()}
+
+    pairs = sum(nk * (nk + 1) / 2 for per in nks for nk in per)        # over layers and batch rows
+    fwd_flop = 4.0 * D * Hq * pairs
+    bwd_flop = 10.0 * D * Hq * pairs
+    attn_ms = phase["fwd"] + phase["bwd"]
+    tflops = (fwd_flop + bwd_flop) / (attn_ms * 1e-3) / 1e12
+    score_flop = 2 * 2.0 * D * Hq * B * L * S * (S + 1) / 2
+
+    # dominant kernel of the step: the backward main kernel (one call = N segments of
+    # prep + main, all on this stream); roofline against the bf16 MFMA peak
+    bwd_call_ms = phase["bwd"] / L
+    bwd_flop_call = bwd_flop / L
+    achieved = bwd_flop_call / (bwd_call_ms * 1e-3) / 1e12
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic_k_bwd_main_c5.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tj = json.load(f)
+        if tj.get("kernel_source_hash") == kernel_source_hash() and tj.get("config") == cfg.name:
+            traffic = tj.get("bytes_per_call")
+    roofline = {"kernel": "k_bwd_main (+k_bwd_prep), one backward call = %d segments" % nseg,
+                "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "algorithmic_flop_per_call": bwd_flop_call, "avg_call_ms": round(bwd_call_ms, 4)}
+
+    copy_ms = None
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        bcopy.copy_(a)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms = c0.elapsed_time(c1)
+        del a, bcopy
+
+    mem = {"max_allocated_gib": round(torch.cuda.max_memory_allocated() / 2**30, 2),
+           "saved_activations_mib_per_layer": round(
+               (B * ncap * Hq * D * (2 if cfg.dtype == "bf16" else 4) + B * Hq * ncap * 4 + B * nkb * 4) / 2**20, 2),
+           "bwd_workspace_mib": round(layers[0]["ws_b"].numel() / 2**20, 2)}
+
+    # ---------------- CPU baseline: the oracle on a bounded sample of the same workload ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, sample_np)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: S={S} B={B} Hq={Hq} Hkv={Hkv} D={D} block={blk} "
+                               f"{cfg.select_mode} {cfg.select_param} layers={L} segments={nseg} "
+                               f"kept={args.kept}",
+                   "global_batch": B, "seq_len": S, "parallelism": "single-gpu"},
+        "pct_bf16_mfma_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
+        "attn_ms_per_step": round(attn_ms, 3),
+        "tokens_per_s_attn": round(B * S / (attn_ms * 1e-3), 1),
+        "tokens_per_s_pipeline": round(B * S / (ms_per_step * 1e-3), 1),
+        "phase_ms_per_step": {kk: round(vv, 3) for kk, vv in phase.items()},
+        "fwd_tflops": round(fwd_flop / (phase["fwd"] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(bwd_flop / (phase["bwd"] * 1e-3) / 1e12, 2),
+        "score_tflops_algorithmic": round(score_flop / (phase["score"] * 1e-3) / 1e12, 2),
+        "kept_tokens_per_layer": nks,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "memory": mem,
+        "input_gen_s": round(gen_s, 1),
+    }
+    if copy_ms is not None:
+        out["copy_1gib_ms"] = round(copy_ms, 4)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, sample, budget_s: float = 12.0):
+    """Oracle fwd+bwd (float64 NumPy, as written) on a bounded sample of the workload: layer 0,
+    kept blocks 0..k-1 (a self-contained causal prefix of the literal top-k set's size), one
+    query head at a time until about budget_s seconds of CPU work have been spent."""
+    import oracle
+    from synth.generate import to_bf16_bits_f32
+    q_all, k_all, v_all, dout_all = sample
+    nb = min(cfg.n_blocks, 128)
+    S_s = nb * cfg.block
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 0) for i in threadpool_info()] + [0]) or os.cpu_count()
+    except Exception:
+        threads = os.cpu_count()
+    kept = np.arange(nb)
+    heads, dt = 0, 0.0
+    while heads < q_all.shape[2] and dt < budget_s:
+        h = heads
+        g = 0 if cfg.n_heads_kv != cfg.n_heads_q else h
+        prep = lambda a, i: np.ascontiguousarray(a[:, :S_s, i:i + 1])
+        q, k, v = prep(q_all, h), prep(k_all, g), prep(v_all, g)
+        if cfg.dtype == "bf16":
+            q, k, v = to_bf16_bits_f32(q), to_bf16_bits_f32(k), to_bf16_bits_f32(v)
+        dout = prep(dout_all, h)
+        t0 = time.time()
+        oracle.attn_fwd_compact(q, k, v, kept, cfg.block)
+        oracle.attn_bwd_compact(q, k, v, kept, cfg.block, dout)
+        dt += time.time() - t0
+        heads += 1
+    Nk = S_s
+    flop = 14.0 * cfg.head_dim * heads * cfg.batch * Nk * (Nk + 1) / 2
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"layer 0, query heads 0..{heads - 1}, kept blocks 0..{nb - 1} ({Nk} kept "
+                      f"tokens, a self-contained causal prefix), attention fwd+bwd in float64 NumPy"}
+
+
+if __name__ == "__main__":
+    main()

@@ -57,7 +57,10 @@ class Inputs:
     dout: np.ndarray         # [B,S,Hq,D] float32 gradient of the loss w.r.t. the final residual
 
 
-def make_layer(cfg: Config, layer: int = 0, seq_len: Optional[int] = None) -> LayerInputs:
+def make_layer(cfg: Config, layer: int = 0, seq_len: Optional[int] = None,
+               round_bf16: bool = True) -> LayerInputs:
+    """One layer's Q/K/V.  round_bf16=False leaves bf16 workloads in float32 for a caller that
+    rounds to bfloat16 itself (torch's cast rounds to nearest even, giving the same bits)."""
     S = cfg.seq_len if seq_len is None else seq_len
     B, Hq, Hkv, D, blk = cfg.batch, cfg.n_heads_q, cfg.n_heads_kv, cfg.head_dim, cfg.block
     nkb = S // blk
@@ -86,7 +89,7 @@ def make_layer(cfg: Config, layer: int = 0, seq_len: Optional[int] = None) -> La
                 k[:, n * blk:(n + 1) * blk, :, :] += shift
     else:
         hh = np.zeros((0,), dtype=np.int64)
-    if cfg.dtype == "bf16":
+    if cfg.dtype == "bf16" and round_bf16:
         q, k, v = to_bf16_bits_f32(q), to_bf16_bits_f32(k), to_bf16_bits_f32(v)
     return LayerInputs(q=q, k=k, v=v, hh_blocks=np.asarray(hh))
 
