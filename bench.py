@@ -114,8 +114,11 @@ def main():
         st["dq"] = torch.zeros((B, S, Hq, D), dtype=torch.float32, device=dev)
         st["dk"] = torch.zeros((B, S, Hkv, D), dtype=torch.float32, device=dev)
         st["dv"] = torch.zeros((B, S, Hkv, D), dtype=torch.float32, device=dev)
-        st["ws_s"] = J.alloc_workspace(J.workspace_bytes(p, J.JENGA_OP_SCORE), dev)
-        st["ws_b"] = J.alloc_workspace(J.workspace_bytes(p, J.JENGA_OP_BWD, maxk, nseg), dev)
+        if l == 0:   # one set of workspaces: the layers run one after another on one stream
+            ws_s = J.alloc_workspace(J.workspace_bytes(p, J.JENGA_OP_SCORE), dev)
+            ws_f = J.alloc_workspace(J.workspace_bytes(p, J.JENGA_OP_FWD, maxk), dev)
+            ws_b = J.alloc_workspace(J.workspace_bytes(p, J.JENGA_OP_BWD, maxk, nseg), dev)
+        st["ws_s"], st["ws_f"], st["ws_b"] = ws_s, ws_f, ws_b
         if args.kept == "scattered":
             kb = random_kept_blocks(nkb, maxk, 5999 + l)
             arr = np.full((B, nkb), -1, np.int32)
@@ -137,7 +140,7 @@ def main():
                 ev[l][2].record(stream)
             ka, na = (st["kept_att"], st["nk_att"]) if args.kept == "scattered" else (st["kept"], st["nk"])
             J.jenga_sparse_attn_fwd(st["p"], st["q"], st["k"], st["v"], ka, na, maxk, resid, st["o"],
-                                    st["lse"])
+                                    st["lse"], st["ws_f"])
             if ev is not None:
                 ev[l][3].record(stream)
         for l in reversed(range(L)):
@@ -199,7 +202,7 @@ def main():
             tj = json.load(f)
         if tj.get("kernel_source_hash") == kernel_source_hash() and tj.get("config") == cfg.name:
             traffic = tj.get("bytes_per_call")
-    roofline = {"kernel": "k_bwd_main (+k_bwd_prep), one backward call = %d segments" % nseg,
+    roofline = {"kernel": "attention backward call (k_dkdv64 + k_dq64 + prologue/pack), %d segments" % nseg,
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                 "algorithmic_flop_per_call": bwd_flop_call, "avg_call_ms": round(bwd_call_ms, 4)}
@@ -220,6 +223,7 @@ def main():
     mem = {"max_allocated_gib": round(torch.cuda.max_memory_allocated() / 2**30, 2),
            "saved_activations_mib_per_layer": round(
                (B * ncap * Hq * D * (2 if cfg.dtype == "bf16" else 4) + B * Hq * ncap * 4 + B * nkb * 4) / 2**20, 2),
+           "fwd_workspace_mib": round(layers[0]["ws_f"].numel() / 2**20, 2),
            "bwd_workspace_mib": round(layers[0]["ws_b"].numel() / 2**20, 2)}
 
     # ---------------- CPU baseline: the oracle on a bounded sample of the same workload ----

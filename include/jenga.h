@@ -76,7 +76,7 @@ const char* jenga_status_string(int status);
 int jenga_topk_count(float keep_ratio, int n_blocks);
 
 /* Workspace bytes needed by `op` (JENGA_OP_SCORE, _FWD or _BWD) for this problem.
- * max_kept_blocks and n_segments only matter for JENGA_OP_BWD.  Returns 0 for an
+ * max_kept_blocks matters for _FWD and _BWD, n_segments for _BWD.  Returns 0 for an
  * invalid problem (and for ops that need no workspace). */
 size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks, int n_segments);
 
@@ -142,10 +142,14 @@ int jenga_select_blocks(const jenga_problem* p, const float* block_scores, int m
  *                      (the saved attention output used by the backward)
  *   lse                [B][Hq][max_kept_blocks*block] fp32, dense, written by kept rank:
  *                      natural-log softmax normaliser of each kept query
+ *   workspace          >= jenga_workspace_bytes(p, JENGA_OP_FWD, max_kept_blocks, 1) bytes,
+ *                      256-byte aligned (bf16: a transposed copy of the kept V rows; fp32
+ *                      needs none and may pass NULL)
  */
 int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, const void* v,
                           const int32_t* kept_idx, const int32_t* n_kept, int max_kept_blocks,
-                          float* resid, void* o_saved, float* lse, void* stream);
+                          float* resid, void* o_saved, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * jenga_sparse_attn_bwd_segmented — backward of jenga_sparse_attn_fwd, computed over

@@ -99,12 +99,18 @@ def test_select_validation(J):
 
 def test_fwd_bwd_validation(J):
     p = _problem(J)
-    fwd = lambda maxk=8, resid=FAKE: J.lib.jenga_sparse_attn_fwd(
-        ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, maxk, resid, FAKE, FAKE, None)
+    fwd = lambda maxk=8, resid=FAKE, ws=FAKE, wsb=1 << 30, pp=p: J.lib.jenga_sparse_attn_fwd(
+        ctypes.byref(pp), FAKE, FAKE, FAKE, FAKE, FAKE, maxk, resid, FAKE, FAKE, ws, wsb, None)
     assert fwd(maxk=0) == J.JENGA_ERR_INVALID_ARG
     assert fwd(maxk=17) == J.JENGA_ERR_INVALID_ARG
     assert fwd(resid=0) == J.JENGA_ERR_INVALID_ARG
     assert fwd(resid=FAKE + 8) == J.JENGA_ERR_INVALID_ARG
+    pb = _problem(J, D=128, dtype=1)                       # bf16 needs a forward workspace
+    need_f = J.workspace_bytes(pb, J.JENGA_OP_FWD, 8)
+    assert need_f > 0
+    assert fwd(pp=pb, ws=0) == J.JENGA_ERR_WORKSPACE
+    assert fwd(pp=pb, wsb=need_f - 1) == J.JENGA_ERR_WORKSPACE
+    assert fwd(pp=pb, ws=FAKE + 16) == J.JENGA_ERR_WORKSPACE
     need = J.workspace_bytes(p, J.JENGA_OP_BWD, 8, 2)
     assert need > 0
     bwd = lambda nseg=2, ws_bytes=need, maxk=8: J.lib.jenga_sparse_attn_bwd_segmented(
@@ -121,6 +127,10 @@ def test_workspace_scales_with_segments_and_kept_blocks(J):
     w1 = J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 1)
     w8 = J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 8)
     w8_half = J.workspace_bytes(p, J.JENGA_OP_BWD, 64, 8)
-    assert w8 * 7 < w1 <= w8 * 8 + 4096
-    assert abs(w8_half * 2 - w8) <= 4096
-    assert J.workspace_bytes(p, J.JENGA_OP_FWD) == 0
+    ktp = 32 * 128 * 128 * 128 * 2                # transposed K tiles: all kept keys
+    seg = lambda L: 32 * L * 4 + 3 * 32 * L * 128 * 2   # D terms, dOut, dOut^T and Q^T tiles
+    assert w1 == ktp + seg(16384)
+    assert w8 == ktp + seg(2048)                  # the per-segment part shrinks as 1/N
+    assert abs(w8_half * 2 - w8) <= 4096          # everything scales with the kept tokens
+    assert J.workspace_bytes(p, J.JENGA_OP_FWD, 128) == ktp
+    assert J.workspace_bytes(_problem(J), J.JENGA_OP_FWD, 8) == 0       # fp32 path needs none

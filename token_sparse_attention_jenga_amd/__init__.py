@@ -65,7 +65,7 @@ def _load() -> ctypes.CDLL:
     lib.jenga_score_blocks.restype = i32
     lib.jenga_select_blocks.argtypes = [P, vp, i32, ctypes.c_float, ctypes.c_uint, vp, vp, vp]
     lib.jenga_select_blocks.restype = i32
-    lib.jenga_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
+    lib.jenga_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.jenga_sparse_attn_fwd.restype = i32
     lib.jenga_sparse_attn_bwd_segmented.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                                                     vp, i32, vp, sz, vp]
@@ -153,10 +153,11 @@ def jenga_select_blocks(p: JengaProblem, block_scores, mode: int, param: float, 
 
 
 def jenga_sparse_attn_fwd(p: JengaProblem, q, k, v, kept_idx, n_kept, max_kept_blocks: int,
-                          resid, o_saved, lse, stream=None) -> None:
+                          resid, o_saved, lse, workspace=None, stream=None) -> None:
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.jenga_sparse_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_idx),
                                    _ptr(n_kept), int(max_kept_blocks), _ptr(resid), _ptr(o_saved),
-                                   _ptr(lse), _stream(stream))
+                                   _ptr(lse), _ptr(workspace), nbytes, _stream(stream))
     _check("jenga_sparse_attn_fwd", st)
 
 
@@ -206,7 +207,8 @@ def sparse_attn_fwd(q, k, v, kept_idx, n_kept, max_kept_blocks: int, block: int,
     ncap = max_kept_blocks * block
     o_saved = torch.empty((B, ncap, Hq, D), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, Hq, ncap), dtype=torch.float32, device=q.device)
-    jenga_sparse_attn_fwd(p, q, k, v, kept_idx, n_kept, max_kept_blocks, resid, o_saved, lse)
+    ws = alloc_workspace(workspace_bytes(p, JENGA_OP_FWD, max_kept_blocks), q.device)
+    jenga_sparse_attn_fwd(p, q, k, v, kept_idx, n_kept, max_kept_blocks, resid, o_saved, lse, ws)
     return o_saved, lse
 
 

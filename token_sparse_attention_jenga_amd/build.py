@@ -14,15 +14,21 @@ LIB = os.path.join(PKG, "libjenga.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "score.hip", "select.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn64.hip", "score.hip", "select.hip", "api.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 
+# Per-file code generation options.  attn64.hip: MFMA results in the VGPR form, so the
+# 64-row-per-wave kernels keep their softmax accumulators in VGPRs and use the AGPR file for
+# the long-lived gradient accumulators instead of spilling to scratch.
+EXTRA = {"attn64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

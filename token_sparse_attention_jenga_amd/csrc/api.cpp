@@ -55,13 +55,37 @@ int seg_len_of(int ncap, int n_segments) {
   return (L + 63) / 64 * 64;
 }
 
-size_t bwd_ws_bytes(const jenga_problem* p, int max_kept_blocks, int n_segments) {
+struct BwdLayout {
+  size_t d, dO, ktp, qtp, dotp, total;
+};
+
+BwdLayout bwd_layout(const jenga_problem* p, int max_kept_blocks, int n_segments) {
   const int ncap = max_kept_blocks * p->block;
   const int L = seg_len_of(ncap, n_segments);
   const size_t es = p->dtype == JENGA_DTYPE_BF16 ? 2 : 4;
-  const size_t d_bytes = (size_t)p->batch * p->n_heads_q * L * sizeof(float);
-  const size_t do_bytes = (size_t)p->batch * L * p->n_heads_q * p->head_dim * es;
-  return align_up(d_bytes) + align_up(do_bytes);
+  const size_t B = p->batch, Hq = p->n_heads_q, Hkv = p->n_heads_kv, D = p->head_dim;
+  BwdLayout o;
+  o.d = 0;
+  o.dO = o.d + align_up(B * Hq * L * sizeof(float));
+  size_t end = o.dO + align_up(B * L * Hq * D * es);
+  o.ktp = o.qtp = o.dotp = end;
+  if (p->dtype == JENGA_DTYPE_BF16) {            // transposed operand tiles of the bf16 path
+    o.ktp = end;
+    o.qtp = o.ktp + align_up(B * Hkv * (size_t)ncap * D * 2);
+    o.dotp = o.qtp + align_up(B * Hq * (size_t)L * D * 2);
+    end = o.dotp + align_up(B * Hq * (size_t)L * D * 2);
+  }
+  o.total = end;
+  return o;
+}
+
+size_t bwd_ws_bytes(const jenga_problem* p, int max_kept_blocks, int n_segments) {
+  return bwd_layout(p, max_kept_blocks, n_segments).total;
+}
+
+size_t fwd_ws_bytes(const jenga_problem* p, int max_kept_blocks) {
+  if (p->dtype != JENGA_DTYPE_BF16) return 0;
+  return align_up((size_t)p->batch * p->n_heads_kv * max_kept_blocks * p->block * p->head_dim * 2);
 }
 
 size_t score_ws_bytes(const jenga_problem* p) {
@@ -98,7 +122,11 @@ int jenga_topk_count(float keep_ratio, int n_blocks) {
 size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks, int n_segments) {
   if (check_problem(p, false) != JENGA_OK) return 0;
   if (op == JENGA_OP_SCORE) return score_ws_bytes(p);
-  if (op == JENGA_OP_FWD) return 0;
+  if (op == JENGA_OP_FWD) {
+    const int nkb = p->seq_len / p->block;
+    if (max_kept_blocks < 1 || max_kept_blocks > nkb) return 0;
+    return fwd_ws_bytes(p, max_kept_blocks);
+  }
   if (op == JENGA_OP_BWD) {
     const int nkb = p->seq_len / p->block;
     if (max_kept_blocks < 1 || max_kept_blocks > nkb || n_segments < 1) return 0;
@@ -165,7 +193,8 @@ int jenga_select_blocks(const jenga_problem* p, const float* block_scores, int m
 
 int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, const void* v,
                           const int32_t* kept_idx, const int32_t* n_kept, int max_kept_blocks,
-                          float* resid, void* o_saved, float* lse, void* stream) {
+                          float* resid, void* o_saved, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   int st = check_problem(p, true);
   if (st != JENGA_OK) return st;
   const int nkb = p->seq_len / p->block;
@@ -174,6 +203,9 @@ int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(resid) || !aligned16(o_saved))
     return JENGA_ERR_INVALID_ARG;
   if (max_kept_blocks < 1 || max_kept_blocks > nkb) return JENGA_ERR_INVALID_ARG;
+  const size_t need = fwd_ws_bytes(p, max_kept_blocks);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0))
+    return JENGA_ERR_WORKSPACE;
   jenga::FwdParams fp;
   fp.q = q;
   fp.k = k;
@@ -195,8 +227,11 @@ int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, 
   fp.max_kept_blocks = max_kept_blocks;
   fp.ncap = max_kept_blocks * p->block;
   fp.scale_log2 = scale_of(p) * 1.4426950408889634f;
-  if (jenga::launch_fwd(fp, p->dtype, p->head_dim, (hipStream_t)stream) != hipSuccess)
-    return JENGA_ERR_LAUNCH;
+  fp.vtp = workspace;
+  const hipError_t e = p->dtype == JENGA_DTYPE_BF16
+                           ? jenga::launch_fwd64(fp, p->head_dim, (hipStream_t)stream)
+                           : jenga::launch_fwd(fp, p->dtype, p->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return JENGA_ERR_LAUNCH;
   return JENGA_OK;
 }
 
@@ -220,6 +255,7 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
     return JENGA_ERR_WORKSPACE;
   const int L = seg_len_of(ncap, n_segments);
+  const BwdLayout lay = bwd_layout(p, max_kept_blocks, n_segments);
   jenga::BwdParams bp;
   bp.q = q;
   bp.k = k;
@@ -235,8 +271,11 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
   bp.dq = dq;
   bp.dk = dk;
   bp.dv = dv;
-  bp.wsD = (float*)workspace;
-  bp.wsdO = (char*)workspace + align_up((size_t)p->batch * p->n_heads_q * L * sizeof(float));
+  bp.wsD = (float*)((char*)workspace + lay.d);
+  bp.wsdO = (char*)workspace + lay.dO;
+  bp.ktp = (char*)workspace + lay.ktp;
+  bp.qtp = (char*)workspace + lay.qtp;
+  bp.dotp = (char*)workspace + lay.dotp;
   bp.B = p->batch;
   bp.S = p->seq_len;
   bp.Hq = p->n_heads_q;
@@ -248,11 +287,15 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
   bp.seg_len = L;
   bp.scale = scale_of(p);
   bp.scale_log2 = bp.scale * 1.4426950408889634f;
+  const bool fast = p->dtype == JENGA_DTYPE_BF16;
+  if (fast && jenga::launch_bwd64_pack_keys(bp, p->head_dim, (hipStream_t)stream) != hipSuccess)
+    return JENGA_ERR_LAUNCH;
   for (int s = 0; s < n_segments; ++s) {
     if ((int64_t)s * L >= ncap) break;
     bp.seg = s;
-    if (jenga::launch_bwd_segment(bp, p->dtype, p->head_dim, (hipStream_t)stream) != hipSuccess)
-      return JENGA_ERR_LAUNCH;
+    const hipError_t e = fast ? jenga::launch_bwd64_segment(bp, p->head_dim, (hipStream_t)stream)
+                              : jenga::launch_bwd_segment(bp, p->dtype, p->head_dim, (hipStream_t)stream);
+    if (e != hipSuccess) return JENGA_ERR_LAUNCH;
   }
   return JENGA_OK;
 }

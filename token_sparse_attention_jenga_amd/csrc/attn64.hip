@@ -1,0 +1,760 @@
+// bf16 token-sparse attention forward and segmented backward for gfx950, 64 rows per wave.
+//
+// Jenga (papercache notes, §4.4): kept rows are addressed in place through the kept-block
+// list (permutation-free token movement), the forward adds its output into the residual in
+// place, and the backward runs segment by segment (segment-based peak cutting).
+//
+// Why 64 rows per wave: with 32 rows, every MFMA operand streamed from LDS feeds 32 rows,
+// i.e. one LDS byte per 32 MFMA flops -- about the measured LDS rate of a CU (~140 B/clk
+// against 4096 flop/clk).  With 64 rows the LDS traffic halves.  The price is register
+// space (two 32x32 accumulator blocks per GEMM), so these kernels run one wave per SIMD with
+// up to 512 VGPRs, two waves per workgroup, and refill LDS asynchronously (direct-to-LDS
+// loads into a second buffer while the current one is consumed).
+//
+// Every MFMA operand is one 16-byte LDS read: operands that reduce over head_dim come from
+// natural tiles; operands that reduce over rows come from TP tiles prepared in global memory
+// (see tiles64.h), so no transpose happens inside the hot loops.
+//
+//   k_pack_tp   kept rows of K / V / Q (head h) -> TP tiles [D][32] in a workspace
+//   k_fwd64     forward:   S^T = K Q^T, online softmax per query (lane-local), O^T += V^T P^T
+//   k_prep64    backward prologue per segment: D_i = dO_i.O_i, dOut -> bf16 natural + TP
+//   k_dkdv64    key-major:  S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q
+//   k_dq64      query-major: S^T = K Q^T, dP^T = V dO^T, dQ += dS K   (no atomics)
+#include "common.h"
+#include "kernels.h"
+#include "tiles64.h"
+
+namespace jenga {
+
+struct PackArgs {
+  const void* src;
+  int64_t s0, s1, s2;        // element strides of src: batch, token, head
+  const int32_t* kept;
+  const int32_t* n_kept;
+  int block, nkb, max_kept_blocks;
+  int rank0, rank_count;     // tiles cover kept ranks [rank0, rank0 + rank_count)
+  int tiles_per_head, H;
+  void* dst;                 // [B][H][tiles_per_head][D][32] bf16
+};
+
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_pack_tp(PackArgs a) {
+  constexpr int PITCH = D + 8;                        // elements; breaks bank aliasing
+  __shared__ bf16 tile[32 * PITCH];
+  const int b = blockIdx.z, h = blockIdx.y, t = blockIdx.x, tid = threadIdx.x;
+  const int32_t* kept = a.kept + (int64_t)b * a.nkb;
+  const int Nk = min(a.n_kept[b], a.max_kept_blocks) * a.block;
+  const int r0 = a.rank0 + 32 * t;
+  const int rend = min(a.rank0 + a.rank_count, Nk);
+  if (r0 >= rend) return;
+  const int pos0 = rank_to_pos(kept, a.block, r0);
+  const bf16* src = (const bf16*)a.src + b * a.s0 + h * a.s2;
+  constexpr int CPR = D / 8;
+  for (int idx = tid; idx < 32 * CPR; idx += 256) {
+    const int row = idx / CPR, c = idx % CPR;
+    *(u32x4*)(tile + row * PITCH + c * 8) = ld16(src + (int64_t)(pos0 + row) * a.s1 + c * 8);
+  }
+  __syncthreads();
+  char* dst = (char*)a.dst + ((((int64_t)b * a.H + h) * a.tiles_per_head + t) * D) * 64;
+  for (int idx = tid; idx < D * 4; idx += 256) {
+    const int d = idx >> 2, c = idx & 3;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(uint16_t, tile[pi16(8 * c + e) * PITCH + d]);
+    u32x4 wv;
+    wv[0] = v[0] | ((uint32_t)v[1] << 16);
+    wv[1] = v[2] | ((uint32_t)v[3] << 16);
+    wv[2] = v[4] | ((uint32_t)v[5] << 16);
+    wv[3] = v[6] | ((uint32_t)v[7] << 16);
+    *(u32x4*)(dst + d * 64 + c * 16) = wv;
+  }
+}
+
+template <int D>
+static hipError_t pack_tp(const PackArgs& a, int B, hipStream_t st) {
+  const int ntiles = (a.rank_count + 31) / 32;
+  if (ntiles <= 0) return hipSuccess;
+  k_pack_tp<D><<<dim3(ntiles, a.H, B), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Forward
+// ------------------------------------------------------------------------------------------
+// Rescaling of the running output is deferred while the running max grows by less than
+// kLazyRescale (log2 units): exp2(z - m) then stays below 2^kLazyRescale, far inside fp32 and
+// bf16 range, and the final normalisation uses the same stale max, so the result is exact.
+constexpr float kLazyRescale = 8.f;
+
+template <int D, int NB, int NW>
+__global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p) {
+  constexpr int RW = 32 * NB, RG = RW * NW;                // rows per wave / per workgroup
+  using C = T64<D>;
+  constexpr int OFF_V = C::NAT32;
+  constexpr int STAGE = C::NAT32 + C::TP32;
+  __shared__ __attribute__((aligned(1024))) char sA[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sB[STAGE];
+  __shared__ int ktab[kKeptTab];
+
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int g = h / (p.Hq / p.Hkv);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
+  const int32_t* kept = p.kept + (int64_t)b * p.nkb;
+  const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
+  const int nqt = (Nk + RG - 1) / RG;
+  if ((int)blockIdx.x >= nqt) return;
+  const int q0 = (nqt - 1 - (int)blockIdx.x) * RG;      // heaviest tiles first
+  const int qw0 = q0 + RW * w;
+  const bool active = qw0 < Nk;                          // Nk is a multiple of 64 >= RW
+  const int qlast = min(q0 + RG, Nk) - 1;
+  const int nsteps = qlast / 32 + 1;
+  stage_kept(ktab, kept, qlast / p.block + 1);
+  __syncthreads();
+  const KeptTab kt{ktab, kept, p.block};
+
+  bf16x8 qf[NB][C::NS];
+  int qpos[NB];
+  if (active) {
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      qpos[qb] = kt.pos(qw0 + 32 * qb + lc);
+      const char* qrow = (const char*)((const bf16*)p.q + b * p.qs[0] + (int64_t)qpos[qb] * p.qs[1] +
+                                       h * p.qs[2]);
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) qf[qb][s] = *(const bf16x8*)(qrow + (16 * s + 8 * hl) * 2);
+    }
+  }
+  f32x16 o[NB][C::NDB];
+#pragma unroll
+  for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) o[qb][db] = zero16();
+  float m_run[NB], l_run[NB];                               // log2 domain
+#pragma unroll
+  for (int qb = 0; qb < NB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
+
+  const char* kbase = (const char*)((const bf16*)p.k + b * p.ks[0] + g * p.ks[2]);
+  const int64_t kstride = p.ks[1] * 2;
+  const char* vtp = (const char*)p.vtp + (((int64_t)b * p.Hkv + g) * (p.ncap / 32)) * C::TP32;
+  const float c2 = p.scale_log2;
+
+  auto issue = [&](int step, char* buf) {
+    const int pos0 = kt.pos(step * 32);
+    dma_nat32<D, NW>(buf, kbase + (int64_t)pos0 * kstride, kstride);
+    dma_tp32<D, NW>(buf + OFF_V, vtp + (int64_t)step * C::TP32);
+  };
+
+  auto compute = [&](int step, const char* buf) {
+    const int kr0 = step * 32;
+    if (!active || kr0 > qw0 + RW - 1) return;
+    const char* Kl = buf;
+    const char* Vl = buf + OFF_V;
+    f32x16 st[NB];
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) st[qb] = zero16();
+    {
+      bf16x8 a = ld_nat<D>(Kl, lc, hl);
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) {
+        const bf16x8 an = s + 1 < C::NS ? ld_nat<D>(Kl, lc, 2 * (s + 1) + hl) : a;
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) st[qb] = Mfma<bf16>::mma(a, qf[qb][s], st[qb]);
+        a = an;
+        if (NB > 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      const int qr = qw0 + 32 * qb + lc;
+      const bool need_mask = kr0 + 31 > qw0 + 32 * qb;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (need_mask && kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) > qr) st[qb][r] = -INFINITY;
+        mx = fmaxf(mx, st[qb][r]);
+      }
+      mx = fmaxf(mx, wave_xor32(mx)) * c2;               // row max in the log2 domain
+      // lazy rescale: move the reference max only when it grows by kLazyRescale or more
+      const bool grow = mx > m_run[qb] + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = fmaxf(m_run[qb], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        l_run[qb] *= alpha;
+        m_run[qb] = m_new;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) o[qb][db] *= alpha;
+      }
+      const float m = m_run[qb];
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qb][r], c2, -m));
+        st[qb][r] = e;
+        rs += e;
+      }
+      l_run[qb] += rs;                                    // lane partial; halves summed at the end
+    }
+    {
+      bf16x8 pf[NB];
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) pf[qb] = frag_from_acc(st[qb], 0);
+      bf16x8 va = ld_tp(Vl, lc, hl);
+#pragma unroll
+      for (int idx = 0; idx < 2 * C::NDB; ++idx) {
+        const int db = idx % C::NDB;
+        const int jn = (idx + 1) / C::NDB, dbn = (idx + 1) % C::NDB;
+        const bf16x8 vn = idx + 1 < 2 * C::NDB ? ld_tp(Vl, dbn * 32 + lc, 2 * jn + hl) : va;
+        if (idx == C::NDB) {
+#pragma unroll
+          for (int qb = 0; qb < NB; ++qb) pf[qb] = frag_from_acc(st[qb], 1);
+        }
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) o[qb][db] = Mfma<bf16>::mma(va, pf[qb], o[qb][db]);
+        va = vn;
+        if (NB > 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  issue(0, sA);
+  wait_all_mem();
+  __syncthreads();
+  for (int step = 0; step < nsteps; step += 2) {
+    if (step + 1 < nsteps) issue(step + 1, sB);
+    compute(step, sA);
+    wait_all_mem();
+    __syncthreads();
+    if (step + 1 >= nsteps) break;
+    if (step + 2 < nsteps) issue(step + 2, sA);
+    compute(step + 1, sB);
+    wait_all_mem();
+    __syncthreads();
+  }
+
+  if (!active) return;
+#pragma unroll
+  for (int qb = 0; qb < NB; ++qb) {
+    const int qr = qw0 + 32 * qb + lc;
+    const float lsum = l_run[qb] + wave_xor32(l_run[qb]);
+    const float inv = 1.f / lsum;
+    float* rrow = p.resid + (((int64_t)b * p.S + qpos[qb]) * p.Hq + h) * D;
+    char* orow = (char*)p.o_saved + ((((int64_t)b * p.ncap + qr) * p.Hq + h) * D) * 2;
+    f32x4 x[C::NDB][4];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) x[db][rg] = *(const f32x4*)(rrow + db * 32 + 8 * rg + 4 * hl);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = db * 32 + 8 * rg + 4 * hl;
+        const float v0 = o[qb][db][4 * rg + 0] * inv, v1 = o[qb][db][4 * rg + 1] * inv;
+        const float v2 = o[qb][db][4 * rg + 2] * inv, v3 = o[qb][db][4 * rg + 3] * inv;
+        f32x4 y = x[db][rg];
+        y[0] += v0;
+        y[1] += v1;
+        y[2] += v2;
+        y[3] += v3;
+        *(f32x4*)(rrow + d0) = y;
+        u32x2 pw;
+        pw[0] = pack_bf16x2(v0, v1);
+        pw[1] = pack_bf16x2(v2, v3);
+        *(u32x2*)(orow + d0 * 2) = pw;
+      }
+    }
+    if (hl == 0) p.lse[((int64_t)b * p.Hq + h) * p.ncap + qr] = (m_run[qb] + log2f(lsum)) * kLn2;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward prologue (one segment): D_i, dOut -> bf16 natural rows and TP tiles
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_prep64(BwdParams p) {
+  constexpr int E = D / 8;                    // elements per thread (8 threads per row)
+  constexpr int PITCH = D + 8;
+  __shared__ bf16 tile[32 * PITCH];
+  const int b = blockIdx.z, h = blockIdx.y, t = blockIdx.x, tid = threadIdx.x;
+  const int32_t* kept = p.kept + (int64_t)b * p.nkb;
+  const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
+  const int qs = p.seg * p.seg_len;
+  const int qe = min(qs + p.seg_len, Nk);
+  const int r0 = qs + 32 * t;
+  if (r0 >= qe) return;                       // qe - qs is a multiple of 64
+  const int pos0 = rank_to_pos(kept, p.block, r0);
+  const int row = tid >> 3, part = tid & 7;
+  const float* drow = p.dout + (((int64_t)b * p.S + pos0 + row) * p.Hq + h) * D + part * E;
+  const char* orow = (const char*)p.o_saved + ((((int64_t)b * p.ncap + r0 + row) * p.Hq + h) * D + part * E) * 2;
+  float dot = 0.f;
+  uint32_t packed[E / 2];
+#pragma unroll
+  for (int c = 0; c < E / 8; ++c) {
+    const u32x4 ow = *(const u32x4*)(orow + c * 16);
+    const f32x4 d0 = *(const f32x4*)(drow + c * 8);
+    const f32x4 d1 = *(const f32x4*)(drow + c * 8 + 4);
+    dot += d0[0] * bf16_lo(ow[0]) + d0[1] * bf16_hi(ow[0]) + d0[2] * bf16_lo(ow[1]) +
+           d0[3] * bf16_hi(ow[1]) + d1[0] * bf16_lo(ow[2]) + d1[1] * bf16_hi(ow[2]) +
+           d1[2] * bf16_lo(ow[3]) + d1[3] * bf16_hi(ow[3]);
+    packed[4 * c + 0] = pack_bf16x2(d0[0], d0[1]);
+    packed[4 * c + 1] = pack_bf16x2(d0[2], d0[3]);
+    packed[4 * c + 2] = pack_bf16x2(d1[0], d1[1]);
+    packed[4 * c + 3] = pack_bf16x2(d1[2], d1[3]);
+  }
+  dot += __shfl_xor(dot, 4, 64);
+  dot += __shfl_xor(dot, 2, 64);
+  dot += __shfl_xor(dot, 1, 64);
+  const int rl = r0 - qs + row;
+  if (part == 0) p.wsD[((int64_t)b * p.Hq + h) * p.seg_len + rl] = dot;
+  char* wrow = (char*)p.wsdO + ((((int64_t)b * p.seg_len + rl) * p.Hq + h) * D + part * E) * 2;
+#pragma unroll
+  for (int c = 0; c < E / 8; ++c) {
+    u32x4 v = {packed[4 * c], packed[4 * c + 1], packed[4 * c + 2], packed[4 * c + 3]};
+    *(u32x4*)(wrow + c * 16) = v;
+    *(u32x4*)(tile + row * PITCH + part * E + c * 8) = v;
+  }
+  __syncthreads();
+  char* dst = (char*)p.dotp + ((((int64_t)b * p.Hq + h) * (p.seg_len / 32) + (r0 - qs) / 32) * D) * 64;
+  for (int idx = tid; idx < D * 4; idx += 256) {
+    const int d = idx >> 2, c = idx & 3;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(uint16_t, tile[pi16(8 * c + e) * PITCH + d]);
+    u32x4 wv;
+    wv[0] = v[0] | ((uint32_t)v[1] << 16);
+    wv[1] = v[2] | ((uint32_t)v[3] << 16);
+    wv[2] = v[4] | ((uint32_t)v[5] << 16);
+    wv[3] = v[6] | ((uint32_t)v[7] << 16);
+    *(u32x4*)(dst + d * 64 + c * 16) = wv;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dK, dV: key-major.  Workgroup = NW waves x 32 kept keys of one KV head.  V is held in
+// registers (B operand of dP = dO V^T) and K in an LDS tile shared by the workgroup (B operand
+// of S = Q K^T), so a wave stays within 256 registers and two waves share each SIMD.
+// ------------------------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p) {
+  using C = T64<D>;
+  constexpr int KEYS = 32 * NW;
+  __shared__ __attribute__((aligned(1024))) char sK[NW * C::NAT32];
+  constexpr int OFF_Q = 0, OFF_DO = C::NAT32, OFF_QT = 2 * C::NAT32, OFF_DOT = 2 * C::NAT32 + C::TP32;
+  constexpr int OFF_LD = 2 * C::NAT32 + 2 * C::TP32;            // lse[32], D[32] (fp32)
+  constexpr int STAGE = OFF_LD + 256;
+  __shared__ __attribute__((aligned(1024))) char sA[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sB[STAGE];
+  __shared__ int ktab[kKeptTab];
+
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int G = p.Hq / p.Hkv;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
+  const int32_t* kept = p.kept + (int64_t)b * p.nkb;
+  const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
+  const int qs = p.seg * p.seg_len;
+  const int qe = min(qs + p.seg_len, Nk);
+  const int k0 = blockIdx.x * KEYS;
+  if (qs >= qe || k0 >= qe) return;
+  const int kw0 = k0 + 32 * w;
+  const bool key_valid = kw0 < Nk;                               // Nk is a multiple of 64
+  stage_kept(ktab, kept, (max(qe, min(k0 + KEYS, Nk)) - 1) / p.block + 1);
+  __syncthreads();
+  const KeptTab kt{ktab, kept, p.block};
+
+  {
+    const char* kbase = (const char*)((const bf16*)p.k + b * p.ks[0] + g * p.ks[2]);
+    const int64_t kstride = p.ks[1] * 2;
+#pragma unroll
+    for (int t = 0; t < NW; ++t)
+      if (k0 + 32 * t < Nk) dma_nat32<D, NW>(sK + t * C::NAT32, kbase + (int64_t)kt.pos(k0 + 32 * t) * kstride, kstride);
+  }
+  const char* Kw = sK + w * C::NAT32;                            // this wave's 32 key rows
+  bf16x8 vf[C::NS];
+  if (key_valid) {
+    const int pos = kt.pos(kw0 + lc);
+    const char* vr = (const char*)((const bf16*)p.v + b * p.vs[0] + (int64_t)pos * p.vs[1] + g * p.vs[2]);
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) vf[s] = *(const bf16x8*)(vr + (16 * s + 8 * hl) * 2);
+  }
+  f32x16 dk[C::NDB], dv[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+
+  const int qstart = max(qs, k0);
+  const int nq = (qe - qstart) / 32;
+  const int nsteps = nq * G;
+  const int64_t qstride = p.qs[1] * 2;
+  const int64_t dostride = (int64_t)p.Hq * D * 2;
+
+  auto issue = [&](int step, char* buf) {
+    const int hh = step / nq;
+    const int q0 = qstart + (step - hh * nq) * 32;
+    const int h = g * G + hh;
+    const int qpos0 = kt.pos(q0);
+    dma_nat32<D, NW>(buf + OFF_Q,
+                     (const char*)((const bf16*)p.q + b * p.qs[0] + h * p.qs[2]) + (int64_t)qpos0 * qstride,
+                     qstride);
+    dma_nat32<D, NW>(buf + OFF_DO,
+                     (const char*)p.wsdO + ((((int64_t)b * p.seg_len + (q0 - qs)) * p.Hq + h) * D) * 2,
+                     dostride);
+    const int64_t tile = ((int64_t)b * p.Hq + h) * (p.seg_len / 32) + (q0 - qs) / 32;
+    dma_tp32<D, NW>(buf + OFF_QT, (const char*)p.qtp + tile * C::TP32);
+    dma_tp32<D, NW>(buf + OFF_DOT, (const char*)p.dotp + tile * C::TP32);
+    if (w == NW - 1 && l < 16) {
+      const float* src = l < 8 ? p.lse + ((int64_t)b * p.Hq + h) * p.ncap + q0 + 4 * l
+                               : p.wsD + ((int64_t)b * p.Hq + h) * p.seg_len + (q0 - qs) + 4 * (l - 8);
+      dma16(src, buf + OFF_LD);
+    }
+  };
+
+  auto compute = [&](int step, const char* buf) {
+    const int hh = step / nq;
+    const int q0 = qstart + (step - hh * nq) * 32;
+    if (!key_valid || q0 + 31 < kw0) return;
+    const char* Ql = buf + OFF_Q;
+    const char* dOl = buf + OFF_DO;
+    const char* QTl = buf + OFF_QT;
+    const char* dOTl = buf + OFF_DOT;
+    const float* lsel = (const float*)(buf + OFF_LD);
+    const float* Dl = lsel + 32;
+    f32x16 sacc = zero16(), pacc = zero16();
+    {
+      bf16x8 aq = ld_nat<D>(Ql, lc, hl), ad = ld_nat<D>(dOl, lc, hl), bk = ld_nat<D>(Kw, lc, hl);
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) {
+        bf16x8 aqn = aq, adn = ad, bkn = bk;
+        if (s + 1 < C::NS) {
+          aqn = ld_nat<D>(Ql, lc, 2 * (s + 1) + hl);
+          adn = ld_nat<D>(dOl, lc, 2 * (s + 1) + hl);
+          bkn = ld_nat<D>(Kw, lc, 2 * (s + 1) + hl);
+        }
+        sacc = Mfma<bf16>::mma(aq, bk, sacc);
+        pacc = Mfma<bf16>::mma(ad, vf[s], pacc);
+        aq = aqn;
+        ad = adn;
+        bk = bkn;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // lane = key kw0 + lc; register r = query q0 + 8(r/4) + 4hl + r%4
+    const bool need_mask = q0 < kw0 + 31;
+    const int kr = kw0 + lc;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const f32x4 lq = *(const f32x4*)(lsel + 8 * rg + 4 * hl);
+      const f32x4 dd = *(const f32x4*)(Dl + 8 * rg + 4 * hl);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * rg + i;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.scale_log2, -lq[i] * kLog2e));
+        if (need_mask && q0 + 8 * rg + 4 * hl + i < kr) pv = 0.f;
+        sacc[r] = pv;
+        pacc[r] = pv * (pacc[r] - dd[i]);
+      }
+    }
+    {
+      bf16x8 pf = frag_from_acc(sacc, 0), sf = frag_from_acc(pacc, 0);
+      bf16x8 bdo = ld_tp(dOTl, lc, hl), bq = ld_tp(QTl, lc, hl);
+#pragma unroll
+      for (int idx = 0; idx < 2 * C::NDB; ++idx) {
+        const int db = idx % C::NDB;
+        const int jn = (idx + 1) / C::NDB, dbn = (idx + 1) % C::NDB;
+        bf16x8 bdon = bdo, bqn = bq;
+        if (idx + 1 < 2 * C::NDB) {
+          bdon = ld_tp(dOTl, dbn * 32 + lc, 2 * jn + hl);
+          bqn = ld_tp(QTl, dbn * 32 + lc, 2 * jn + hl);
+        }
+        if (idx == C::NDB) {
+          pf = frag_from_acc(sacc, 1);
+          sf = frag_from_acc(pacc, 1);
+        }
+        dv[db] = Mfma<bf16>::mma(pf, bdo, dv[db]);
+        dk[db] = Mfma<bf16>::mma(sf, bq, dk[db]);
+        bdo = bdon;
+        bq = bqn;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    issue(0, sA);
+    wait_all_mem();
+    __syncthreads();
+    for (int step = 0; step < nsteps; step += 2) {
+      if (step + 1 < nsteps) issue(step + 1, sB);
+      compute(step, sA);
+      wait_all_mem();
+      __syncthreads();
+      if (step + 1 >= nsteps) break;
+      if (step + 2 < nsteps) issue(step + 2, sA);
+      compute(step + 1, sB);
+      wait_all_mem();
+      __syncthreads();
+    }
+  }
+
+  if (!key_valid) return;
+  // dK (scaled), dV += accumulators; lane holds head_dim column db*32 + lc of keys
+  // kw0 + 8(r/4) + 4hl + r%4.  Reads are batched per 4-register group.
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) {
+    float* dkr[4];
+    float* dvr[4];
+    float xk[4][C::NDB], xv[4][C::NDB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pos = kt.pos(kw0 + 8 * rg + 4 * hl + i);
+      dkr[i] = p.dk + (((int64_t)b * p.S + pos) * p.Hkv + g) * D + lc;
+      dvr[i] = p.dv + (((int64_t)b * p.S + pos) * p.Hkv + g) * D + lc;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        xk[i][db] = dkr[i][db * 32];
+        xv[i][db] = dvr[i][db * 32];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        dkr[i][db * 32] = xk[i][db] + p.scale * dk[db][4 * rg + i];
+        dvr[i][db * 32] = xv[i][db] + dv[db][4 * rg + i];
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dQ: query-major.  Workgroup = 2 waves x 64 kept queries of one query head.
+// ------------------------------------------------------------------------------------------
+template <int D, int NB, int NW>
+__global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) {
+  constexpr int RW = 32 * NB, RG = RW * NW;
+  using C = T64<D>;
+  constexpr int OFF_K = 0, OFF_V = C::NAT32, OFF_KT = 2 * C::NAT32;
+  constexpr int STAGE = 2 * C::NAT32 + C::TP32;
+  __shared__ __attribute__((aligned(1024))) char sA[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sB[STAGE];
+  __shared__ int ktab[kKeptTab];
+
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int g = h / (p.Hq / p.Hkv);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
+  const int32_t* kept = p.kept + (int64_t)b * p.nkb;
+  const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
+  const int qs = p.seg * p.seg_len;
+  const int qe = min(qs + p.seg_len, Nk);
+  const int nqt = (qe - qs + RG - 1) / RG;
+  if (qs >= qe || (int)blockIdx.x >= nqt) return;
+  const int q0 = qs + (nqt - 1 - (int)blockIdx.x) * RG;         // heaviest tiles first
+  const int qw0 = q0 + RW * w;
+  const bool active = qw0 < qe;                                  // qe - qs multiple of 64
+  const int qlast = min(q0 + RG, qe) - 1;
+  const int nsteps = qlast / 32 + 1;
+  stage_kept(ktab, kept, qlast / p.block + 1);
+  __syncthreads();
+  const KeptTab kt{ktab, kept, p.block};
+
+  bf16x8 qf[NB][C::NS], df[NB][C::NS];
+  float lse2[NB], Dv[NB];
+  if (active) {
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      const int qr = qw0 + 32 * qb + lc;
+      const int qpos = kt.pos(qr);
+      const char* qrow = (const char*)((const bf16*)p.q + b * p.qs[0] + (int64_t)qpos * p.qs[1] + h * p.qs[2]);
+      const char* drow = (const char*)p.wsdO + ((((int64_t)b * p.seg_len + (qr - qs)) * p.Hq + h) * D) * 2;
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) {
+        qf[qb][s] = *(const bf16x8*)(qrow + (16 * s + 8 * hl) * 2);
+        df[qb][s] = *(const bf16x8*)(drow + (16 * s + 8 * hl) * 2);
+      }
+      lse2[qb] = p.lse[((int64_t)b * p.Hq + h) * p.ncap + qr] * kLog2e;
+      Dv[qb] = p.wsD[((int64_t)b * p.Hq + h) * p.seg_len + (qr - qs)];
+    }
+  }
+  f32x16 acc[NB][C::NDB];
+#pragma unroll
+  for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) acc[qb][db] = zero16();
+
+  const char* kbase = (const char*)((const bf16*)p.k + b * p.ks[0] + g * p.ks[2]);
+  const char* vbase = (const char*)((const bf16*)p.v + b * p.vs[0] + g * p.vs[2]);
+  const int64_t kstride = p.ks[1] * 2, vstride = p.vs[1] * 2;
+  const char* ktp = (const char*)p.ktp + (((int64_t)b * p.Hkv + g) * (p.ncap / 32)) * C::TP32;
+
+  auto issue = [&](int step, char* buf) {
+    const int pos0 = kt.pos(step * 32);
+    dma_nat32<D, NW>(buf + OFF_K, kbase + (int64_t)pos0 * kstride, kstride);
+    dma_nat32<D, NW>(buf + OFF_V, vbase + (int64_t)pos0 * vstride, vstride);
+    dma_tp32<D, NW>(buf + OFF_KT, ktp + (int64_t)step * C::TP32);
+  };
+
+  auto compute = [&](int step, const char* buf) {
+    const int kr0 = step * 32;
+    if (!active || kr0 > qw0 + RW - 1) return;
+    const char* Kl = buf + OFF_K;
+    const char* Vl = buf + OFF_V;
+    const char* KTl = buf + OFF_KT;
+    f32x16 st[NB], dp[NB];
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      st[qb] = zero16();
+      dp[qb] = zero16();
+    }
+    {
+      bf16x8 ak = ld_nat<D>(Kl, lc, hl), av = ld_nat<D>(Vl, lc, hl);
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) {
+        bf16x8 akn = ak, avn = av;
+        if (s + 1 < C::NS) {
+          akn = ld_nat<D>(Kl, lc, 2 * (s + 1) + hl);
+          avn = ld_nat<D>(Vl, lc, 2 * (s + 1) + hl);
+        }
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) {
+          st[qb] = Mfma<bf16>::mma(ak, qf[qb][s], st[qb]);
+          dp[qb] = Mfma<bf16>::mma(av, df[qb][s], dp[qb]);
+        }
+        ak = akn;
+        av = avn;
+        if (NB > 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      const int qr = qw0 + 32 * qb + lc;
+      const bool need_mask = kr0 + 31 > qw0 + 32 * qb;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qb][r], p.scale_log2, -lse2[qb]));
+        if (need_mask && kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) > qr) pv = 0.f;
+        st[qb][r] = pv * (dp[qb][r] - Dv[qb]);
+      }
+    }
+    {
+      bf16x8 af[NB];
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) af[qb] = frag_from_acc(st[qb], 0);
+      bf16x8 bk = ld_tp(KTl, lc, hl);
+#pragma unroll
+      for (int idx = 0; idx < 2 * C::NDB; ++idx) {
+        const int db = idx % C::NDB;
+        const int jn = (idx + 1) / C::NDB, dbn = (idx + 1) % C::NDB;
+        const bf16x8 bkn = idx + 1 < 2 * C::NDB ? ld_tp(KTl, dbn * 32 + lc, 2 * jn + hl) : bk;
+        if (idx == C::NDB) {
+#pragma unroll
+          for (int qb = 0; qb < NB; ++qb) af[qb] = frag_from_acc(st[qb], 1);
+        }
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) acc[qb][db] = Mfma<bf16>::mma(af[qb], bk, acc[qb][db]);
+        bk = bkn;
+        if (NB > 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  issue(0, sA);
+  wait_all_mem();
+  __syncthreads();
+  for (int step = 0; step < nsteps; step += 2) {
+    if (step + 1 < nsteps) issue(step + 1, sB);
+    compute(step, sA);
+    wait_all_mem();
+    __syncthreads();
+    if (step + 1 >= nsteps) break;
+    if (step + 2 < nsteps) issue(step + 2, sA);
+    compute(step + 1, sB);
+    wait_all_mem();
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // dQ accumulator: lane holds head_dim column db*32 + lc of queries 8(r/4)+4hl+r%4
+#pragma unroll
+  for (int qb = 0; qb < NB; ++qb) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      float* dqr[4];
+      float x[4][C::NDB];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = kt.pos(qw0 + 32 * qb + 8 * rg + 4 * hl + i);
+        dqr[i] = p.dq + (((int64_t)b * p.S + pos) * p.Hq + h) * D + lc;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) x[i][db] = dqr[i][db * 32];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) dqr[i][db * 32] = x[i][db] + p.scale * acc[qb][db][4 * rg + i];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Shapes: *_NB 32-row blocks per wave, *_NW waves per workgroup.
+constexpr int FWD_NB = 1, FWD_NW = 4;
+constexpr int DKDV_NW = 8;
+constexpr int DQ_NB = 1, DQ_NW = 4;
+
+template <int D>
+static hipError_t launch_fwd64_t(const FwdParams& p, hipStream_t st) {
+  PackArgs a{p.v, p.vs[0], p.vs[1], p.vs[2], p.kept, p.n_kept, p.block, p.nkb, p.max_kept_blocks,
+             0, p.ncap, p.ncap / 32, p.Hkv, p.vtp};
+  hipError_t e = pack_tp<D>(a, p.B, st);
+  if (e != hipSuccess) return e;
+  constexpr int RG = 32 * FWD_NB * FWD_NW;
+  k_fwd64<D, FWD_NB, FWD_NW><<<dim3((p.ncap + RG - 1) / RG, p.Hq, p.B), 64 * FWD_NW, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd64(const FwdParams& p, int D, hipStream_t st) {
+  return D == 64 ? launch_fwd64_t<64>(p, st) : launch_fwd64_t<128>(p, st);
+}
+
+template <int D>
+static hipError_t pack_keys_t(const BwdParams& p, hipStream_t st) {
+  PackArgs a{p.k, p.ks[0], p.ks[1], p.ks[2], p.kept, p.n_kept, p.block, p.nkb, p.max_kept_blocks,
+             0, p.ncap, p.ncap / 32, p.Hkv, p.ktp};
+  return pack_tp<D>(a, p.B, st);
+}
+
+hipError_t launch_bwd64_pack_keys(const BwdParams& p, int D, hipStream_t st) {
+  return D == 64 ? pack_keys_t<64>(p, st) : pack_keys_t<128>(p, st);
+}
+
+template <int D>
+static hipError_t bwd64_segment_t(const BwdParams& p, hipStream_t st) {
+  const int L = p.seg_len;
+  const int seg_cap = min(L, p.ncap - p.seg * L);          // ranks of this segment (capacity)
+  if (seg_cap <= 0) return hipSuccess;
+  k_prep64<D><<<dim3((seg_cap + 31) / 32, p.Hq, p.B), 256, 0, st>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  PackArgs a{p.q, p.qs[0], p.qs[1], p.qs[2], p.kept, p.n_kept, p.block, p.nkb, p.max_kept_blocks,
+             p.seg * L, seg_cap, L / 32, p.Hq, p.qtp};
+  e = pack_tp<D>(a, p.B, st);
+  if (e != hipSuccess) return e;
+  const int seg_end = p.seg * L + seg_cap;
+  constexpr int KG = 32 * DKDV_NW;
+  k_dkdv32<D, DKDV_NW><<<dim3((seg_end + KG - 1) / KG, p.Hkv, p.B), 64 * DKDV_NW, 0, st>>>(p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int QG = 32 * DQ_NB * DQ_NW;
+  k_dq64<D, DQ_NB, DQ_NW><<<dim3((seg_cap + QG - 1) / QG, p.Hq, p.B), 64 * DQ_NW, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd64_segment(const BwdParams& p, int D, hipStream_t st) {
+  return D == 64 ? bwd64_segment_t<64>(p, st) : bwd64_segment_t<128>(p, st);
+}
+
+}  // namespace jenga

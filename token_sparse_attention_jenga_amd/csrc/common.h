@@ -52,14 +52,14 @@ __device__ inline f32x16 zero16() {
   return z;
 }
 
-// Round-to-nearest-even float -> bf16 bits (inputs are finite).
-__device__ inline uint32_t bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// float -> bf16 with round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -67,12 +67,8 @@ __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0
 // Eight fp32 values -> one bf16x8 MFMA operand.
 __device__ inline bf16x8 to_frag8(float a0, float a1, float a2, float a3, float a4, float a5,
                                   float a6, float a7) {
-  u32x4 w;
-  w[0] = pack_bf16x2(a0, a1);
-  w[1] = pack_bf16x2(a2, a3);
-  w[2] = pack_bf16x2(a4, a5);
-  w[3] = pack_bf16x2(a6, a7);
-  return __builtin_bit_cast(bf16x8, w);
+  const f32x8 v = {a0, a1, a2, a3, a4, a5, a6, a7};
+  return __builtin_convertvector(v, bf16x8);
 }
 
 // LDS transpose read of 16-bit data (gfx950).  Within every group of 16 lanes, lane j

@@ -36,6 +36,7 @@ struct FwdParams {
   float* resid;
   void* o_saved;
   float* lse;
+  void* vtp;     // bf16 path: workspace [B][Hkv][ncap/32] TP tiles of the kept V rows
   int B, S, Hq, Hkv, block, nkb, max_kept_blocks, ncap;
   float scale_log2;
 };
@@ -55,6 +56,9 @@ struct BwdParams {
   float* dv;
   float* wsD;    // [B][Hq][L]   dot(dO, O) of the segment's queries
   void* wsdO;    // [B][L][Hq][D] dOut rows of the segment in operand dtype, by kept rank
+  void* ktp;     // bf16 path: [B][Hkv][ncap/32] TP tiles of the kept K rows
+  void* qtp;     // bf16 path: [B][Hq][L/32] TP tiles of the segment's Q rows
+  void* dotp;    // bf16 path: [B][Hq][L/32] TP tiles of the segment's dOut rows (bf16)
   int B, S, Hq, Hkv, block, nkb, max_kept_blocks, ncap, seg_len, seg;
   float scale, scale_log2;
 };
@@ -64,5 +68,10 @@ hipError_t launch_score(const ScoreParams& p, int dtype, int D, hipStream_t st);
 hipError_t launch_select(const SelectParams& p, hipStream_t st);
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, hipStream_t st);
 hipError_t launch_bwd_segment(const BwdParams& p, int dtype, int D, hipStream_t st);
+
+// bf16 kernels with 64 rows per wave (attn64.hip)
+hipError_t launch_fwd64(const FwdParams& p, int D, hipStream_t st);
+hipError_t launch_bwd64_pack_keys(const BwdParams& p, int D, hipStream_t st);
+hipError_t launch_bwd64_segment(const BwdParams& p, int D, hipStream_t st);
 
 }  // namespace jenga

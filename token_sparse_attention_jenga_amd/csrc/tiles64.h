@@ -1,0 +1,104 @@
+// Tile plumbing for the bf16 kernels that give each wave 64 rows (two 32-row MFMA blocks).
+//
+// Two LDS tile forms, both filled with gfx950 direct-to-LDS loads (global_load_lds_dwordx4:
+// lane i of a wave writes its 16 bytes at LDS base + 16*i, from any global address):
+//   natural tile  [32 rows][D] bf16, 16-byte chunk c of row r stored at chunk c ^ (r & 7);
+//                 read as MFMA operands whose reduction runs along head_dim.
+//   TP tile       [D][32 positions] bf16: row r of the source tile sits at position pi(r),
+//                 pi swapping bits 2 and 3 of r.  Chunk c of line d stored at c ^ ((d>>2)&3).
+//                 One 16-byte read at line d, chunk 2j + h gives the 8 source rows that lane
+//                 half h needs for k-step j when the other operand comes straight from a
+//                 32x32 accumulator (registers 8j..8j+7 hold rows 16j + pi(8h + i)).
+// TP tiles are produced in global memory by k_pack_tp / the backward prologue, so the hot
+// kernels only copy them.
+#pragma once
+
+#include "common.h"
+
+namespace jenga {
+
+__host__ __device__ constexpr int pi16(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+template <int D>
+struct T64 {
+  static constexpr int ROWB = D * 2;       // natural row bytes
+  static constexpr int CPR = ROWB / 16;    // 16-byte chunks per natural row
+  static constexpr int NAT32 = 32 * ROWB;  // natural 32-row tile bytes
+  static constexpr int TP32 = D * 64;      // TP tile bytes
+  static constexpr int NS = D / 16;        // MFMA k-steps over head_dim
+  static constexpr int NDB = D / 32;       // 32-wide head_dim blocks
+};
+
+__device__ inline void dma16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)lds, 16, 0, 0);
+}
+
+// Wait for every outstanding memory operation of this wave (direct-to-LDS loads included).
+__device__ inline void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Natural 32-row tile: rows at g_row0 + r * row_stride (bytes).  NW waves share the copy.
+template <int D, int NW>
+__device__ inline void dma_nat32(char* lds_tile, const char* g_row0, int64_t row_stride) {
+  constexpr int CPR = T64<D>::CPR;
+  constexpr int NI = 32 * CPR / 64;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+  for (int n = w; n < NI; n += NW) {
+    const int idx = n * 64 + l;
+    const int row = idx / CPR, phys = idx % CPR;
+    const int c = phys ^ (row & 7);
+    dma16(g_row0 + row * row_stride + c * 16, lds_tile + n * 1024);
+  }
+}
+
+// TP tile: a contiguous [D][32] bf16 block in global memory.
+template <int D, int NW>
+__device__ inline void dma_tp32(char* lds_tile, const char* g_tile) {
+  constexpr int NI = D * 64 / 1024;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+  for (int n = w; n < NI; n += NW) {
+    const int idx = n * 64 + l;
+    const int d = idx >> 2, phys = idx & 3;
+    const int c = phys ^ ((d >> 2) & 3);
+    dma16(g_tile + d * 64 + c * 16, lds_tile + n * 1024);
+  }
+}
+
+template <int D>
+__device__ inline bf16x8 ld_nat(const char* tile, int row, int c) {
+  return *(const bf16x8*)(tile + row * T64<D>::ROWB + ((c ^ (row & 7)) << 4));
+}
+
+__device__ inline bf16x8 ld_tp(const char* tile, int d, int c) {
+  return *(const bf16x8*)(tile + d * 64 + ((c ^ ((d >> 2) & 3)) << 4));
+}
+
+// Kept-block table staged in LDS once per workgroup, so the hot loops resolve a kept rank to
+// its token position without a global-memory round trip.  Blocks beyond the table's capacity
+// fall back to the global list.
+constexpr int kKeptTab = 2048;
+
+struct KeptTab {
+  const int* s;            // LDS copy of kept[0 .. min(n, kKeptTab))
+  const int32_t* g;        // the global list
+  int block;
+  __device__ int pos(int r) const {
+    const int kb = r / block;
+    return (kb < kKeptTab ? s[kb] : g[kb]) * block + (r - kb * block);
+  }
+};
+
+// All threads of the workgroup: copy kept[0..nb) (clipped to the table) into LDS.  The caller
+// synchronises before the first lookup.
+__device__ inline void stage_kept(int* tab, const int32_t* kept, int nb) {
+  const int n = min(nb, kKeptTab);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) tab[i] = kept[i];
+}
+
+__device__ inline bf16x8 frag_from_acc(const f32x16& a, int j) {
+  return to_frag8(a[8 * j + 0], a[8 * j + 1], a[8 * j + 2], a[8 * j + 3], a[8 * j + 4],
+                  a[8 * j + 5], a[8 * j + 6], a[8 * j + 7]);
+}
+
+}  // namespace jenga
