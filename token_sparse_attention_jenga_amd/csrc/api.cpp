@@ -56,7 +56,7 @@ int seg_len_of(int ncap, int n_segments) {
 }
 
 struct BwdLayout {
-  size_t d, dO, ktp, qtp, dotp, total;
+  size_t d, l2, dO, ktp, qtp, dotp, total;
 };
 
 BwdLayout bwd_layout(const jenga_problem* p, int max_kept_blocks, int n_segments) {
@@ -66,7 +66,8 @@ BwdLayout bwd_layout(const jenga_problem* p, int max_kept_blocks, int n_segments
   const size_t B = p->batch, Hq = p->n_heads_q, Hkv = p->n_heads_kv, D = p->head_dim;
   BwdLayout o;
   o.d = 0;
-  o.dO = o.d + align_up(B * Hq * L * sizeof(float));
+  o.l2 = o.d + align_up(B * Hq * L * sizeof(float));
+  o.dO = o.l2 + (p->dtype == JENGA_DTYPE_BF16 ? align_up(B * Hq * L * sizeof(float)) : 0);
   size_t end = o.dO + align_up(B * L * Hq * D * es);
   o.ktp = o.qtp = o.dotp = end;
   if (p->dtype == JENGA_DTYPE_BF16) {            // transposed operand tiles of the bf16 path
@@ -272,6 +273,7 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
   bp.dk = dk;
   bp.dv = dv;
   bp.wsD = (float*)((char*)workspace + lay.d);
+  bp.wsL2 = (float*)((char*)workspace + lay.l2);
   bp.wsdO = (char*)workspace + lay.dO;
   bp.ktp = (char*)workspace + lay.ktp;
   bp.qtp = (char*)workspace + lay.qtp;

@@ -93,8 +93,11 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
   using C = T64<D>;
   constexpr int OFF_V = C::NAT32;
   constexpr int STAGE = C::NAT32 + C::TP32;
+  using DC = DmaCount<D, NW>;
+  constexpr int PER = DC::NAT_W + DC::TP_W;     // direct-to-LDS instructions per wave per step
   __shared__ __attribute__((aligned(1024))) char sA[STAGE];
   __shared__ __attribute__((aligned(1024))) char sB[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sC[STAGE];
   __shared__ int ktab[kKeptTab];
 
   const int b = blockIdx.z, h = blockIdx.y;
@@ -141,11 +144,16 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
   const int64_t kstride = p.ks[1] * 2;
   const char* vtp = (const char*)p.vtp + (((int64_t)b * p.Hkv + g) * (p.ncap / 32)) * C::TP32;
   const float c2 = p.scale_log2;
+  NatPlan<D, NW> kplan;
+  kplan.init(kstride);
+  TpPlan<D, NW> vplan;
+  vplan.init();
+  ReadPlan<D> rp;
+  rp.init();
 
   auto issue = [&](int step, char* buf) {
-    const int pos0 = kt.pos(step * 32);
-    dma_nat32<D, NW>(buf, kbase + (int64_t)pos0 * kstride, kstride);
-    dma_tp32<D, NW>(buf + OFF_V, vtp + (int64_t)step * C::TP32);
+    kplan.issue(buf, kbase + (int64_t)kt.pos(step * 32) * kstride);
+    vplan.issue(buf + OFF_V, vtp + (int64_t)step * C::TP32);
   };
 
   auto compute = [&](int step, const char* buf) {
@@ -156,27 +164,23 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
     f32x16 st[NB];
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) st[qb] = zero16();
-    {
-      bf16x8 a = ld_nat<D>(Kl, lc, hl);
 #pragma unroll
-      for (int s = 0; s < C::NS; ++s) {
-        const bf16x8 an = s + 1 < C::NS ? ld_nat<D>(Kl, lc, 2 * (s + 1) + hl) : a;
+    for (int s = 0; s < C::NS; ++s) {
+      const bf16x8 a = ldo(Kl, rp.nat[s]);
 #pragma unroll
-        for (int qb = 0; qb < NB; ++qb) st[qb] = Mfma<bf16>::mma(a, qf[qb][s], st[qb]);
-        a = an;
-        if (NB > 1) __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int qb = 0; qb < NB; ++qb) st[qb] = Mfma<bf16>::mma(a, qf[qb][s], st[qb]);
     }
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      const int qr = qw0 + 32 * qb + lc;
-      const bool need_mask = kr0 + 31 > qw0 + 32 * qb;
-      float mx = -INFINITY;
+      if (kr0 + 31 > qw0 + 32 * qb) {                      // diagonal step: causal mask
+        const int qr = qw0 + 32 * qb + lc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (need_mask && kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) > qr) st[qb][r] = -INFINITY;
-        mx = fmaxf(mx, st[qb][r]);
+        for (int r = 0; r < 16; ++r)
+          if (kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) > qr) st[qb][r] = -INFINITY;
       }
+      float mx = st[qb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[qb][r]);
       mx = fmaxf(mx, wave_xor32(mx)) * c2;               // row max in the log2 domain
       // lazy rescale: move the reference max only when it grows by kLazyRescale or more
       const bool grow = mx > m_run[qb] + kLazyRescale;
@@ -198,41 +202,36 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
       }
       l_run[qb] += rs;                                    // lane partial; halves summed at the end
     }
-    {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
       bf16x8 pf[NB];
 #pragma unroll
-      for (int qb = 0; qb < NB; ++qb) pf[qb] = frag_from_acc(st[qb], 0);
-      bf16x8 va = ld_tp(Vl, lc, hl);
+      for (int qb = 0; qb < NB; ++qb) pf[qb] = frag_from_acc(st[qb], j);
 #pragma unroll
-      for (int idx = 0; idx < 2 * C::NDB; ++idx) {
-        const int db = idx % C::NDB;
-        const int jn = (idx + 1) / C::NDB, dbn = (idx + 1) % C::NDB;
-        const bf16x8 vn = idx + 1 < 2 * C::NDB ? ld_tp(Vl, dbn * 32 + lc, 2 * jn + hl) : va;
-        if (idx == C::NDB) {
-#pragma unroll
-          for (int qb = 0; qb < NB; ++qb) pf[qb] = frag_from_acc(st[qb], 1);
-        }
+      for (int db = 0; db < C::NDB; ++db) {
+        const bf16x8 va = ldo(Vl + db * 2048, rp.tp[j]);
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb) o[qb][db] = Mfma<bf16>::mma(va, pf[qb], o[qb][db]);
-        va = vn;
-        if (NB > 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
+  // three-buffer ring: the tiles of step t+2 load while step t computes
+  auto stage = [&](int t, const char* cur, char* nxt) {
+    if (!DC::EXACT || t + 1 >= nsteps) wait_all_mem();
+    else wait_vm<PER>();
+    __syncthreads();
+    if (t + 2 < nsteps) issue(t + 2, nxt);
+    compute(t, cur);
+  };
   issue(0, sA);
-  wait_all_mem();
-  __syncthreads();
-  for (int step = 0; step < nsteps; step += 2) {
-    if (step + 1 < nsteps) issue(step + 1, sB);
-    compute(step, sA);
-    wait_all_mem();
-    __syncthreads();
-    if (step + 1 >= nsteps) break;
-    if (step + 2 < nsteps) issue(step + 2, sA);
-    compute(step + 1, sB);
-    wait_all_mem();
-    __syncthreads();
+  if (nsteps > 1) issue(1, sB);
+  for (int t = 0; t < nsteps; t += 3) {
+    stage(t, sA, sC);
+    if (t + 1 >= nsteps) break;
+    stage(t + 1, sB, sA);
+    if (t + 2 >= nsteps) break;
+    stage(t + 2, sC, sB);
   }
 
   if (!active) return;
@@ -309,7 +308,10 @@ __global__ __launch_bounds__(256) void k_prep64(BwdParams p) {
   dot += __shfl_xor(dot, 2, 64);
   dot += __shfl_xor(dot, 1, 64);
   const int rl = r0 - qs + row;
-  if (part == 0) p.wsD[((int64_t)b * p.Hq + h) * p.seg_len + rl] = dot;
+  if (part == 0) {
+    p.wsD[((int64_t)b * p.Hq + h) * p.seg_len + rl] = dot;
+    p.wsL2[((int64_t)b * p.Hq + h) * p.seg_len + rl] = p.lse[((int64_t)b * p.Hq + h) * p.ncap + r0 + row] * kLog2e;
+  }
   char* wrow = (char*)p.wsdO + ((((int64_t)b * p.seg_len + rl) * p.Hq + h) * D + part * E) * 2;
 #pragma unroll
   for (int c = 0; c < E / 8; ++c) {
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
   constexpr int KEYS = 32 * NW;
   __shared__ __attribute__((aligned(1024))) char sK[NW * C::NAT32];
   constexpr int OFF_Q = 0, OFF_DO = C::NAT32, OFF_QT = 2 * C::NAT32, OFF_DOT = 2 * C::NAT32 + C::TP32;
-  constexpr int OFF_LD = 2 * C::NAT32 + 2 * C::TP32;            // lse[32], D[32] (fp32)
+  constexpr int OFF_LD = 2 * C::NAT32 + 2 * C::TP32;            // lse2[32], D[32] (fp32)
   constexpr int STAGE = OFF_LD + 256;
   __shared__ __attribute__((aligned(1024))) char sA[STAGE];
   __shared__ __attribute__((aligned(1024))) char sB[STAGE];
@@ -365,12 +367,15 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
   __syncthreads();
   const KeptTab kt{ktab, kept, p.block};
 
+  const int64_t kstride = p.ks[1] * 2, qstride = p.qs[1] * 2;
+  const int64_t dostride = (int64_t)p.Hq * D * 2;
   {
+    NatPlan<D, NW> kp;
+    kp.init(kstride);
     const char* kbase = (const char*)((const bf16*)p.k + b * p.ks[0] + g * p.ks[2]);
-    const int64_t kstride = p.ks[1] * 2;
 #pragma unroll
     for (int t = 0; t < NW; ++t)
-      if (k0 + 32 * t < Nk) dma_nat32<D, NW>(sK + t * C::NAT32, kbase + (int64_t)kt.pos(k0 + 32 * t) * kstride, kstride);
+      if (k0 + 32 * t < Nk) kp.issue(sK + t * C::NAT32, kbase + (int64_t)kt.pos(k0 + 32 * t) * kstride);
   }
   const char* Kw = sK + w * C::NAT32;                            // this wave's 32 key rows
   bf16x8 vf[C::NS];
@@ -390,27 +395,32 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
   const int qstart = max(qs, k0);
   const int nq = (qe - qstart) / 32;
   const int nsteps = nq * G;
-  const int64_t qstride = p.qs[1] * 2;
-  const int64_t dostride = (int64_t)p.Hq * D * 2;
+  NatPlan<D, NW> qplan, dplan;
+  qplan.init(qstride);
+  dplan.init(dostride);
+  TpPlan<D, NW> tplan;
+  tplan.init();
+  ReadPlan<D> rp;
+  rp.init();
+  // lse2 / D rows of a step: 256 bytes = 16 chunks, LDC per wave
+  constexpr int LDC = 16 / NW;
+  static_assert(16 % NW == 0, "lse/D chunks must split evenly over the waves");
+  const int ld_chunk = LDC * w + l;
 
   auto issue = [&](int step, char* buf) {
     const int hh = step / nq;
     const int q0 = qstart + (step - hh * nq) * 32;
     const int h = g * G + hh;
-    const int qpos0 = kt.pos(q0);
-    dma_nat32<D, NW>(buf + OFF_Q,
-                     (const char*)((const bf16*)p.q + b * p.qs[0] + h * p.qs[2]) + (int64_t)qpos0 * qstride,
-                     qstride);
-    dma_nat32<D, NW>(buf + OFF_DO,
-                     (const char*)p.wsdO + ((((int64_t)b * p.seg_len + (q0 - qs)) * p.Hq + h) * D) * 2,
-                     dostride);
+    qplan.issue(buf + OFF_Q, (const char*)((const bf16*)p.q + b * p.qs[0] + h * p.qs[2]) +
+                                 (int64_t)kt.pos(q0) * qstride);
+    dplan.issue(buf + OFF_DO, (const char*)p.wsdO + ((((int64_t)b * p.seg_len + (q0 - qs)) * p.Hq + h) * D) * 2);
     const int64_t tile = ((int64_t)b * p.Hq + h) * (p.seg_len / 32) + (q0 - qs) / 32;
-    dma_tp32<D, NW>(buf + OFF_QT, (const char*)p.qtp + tile * C::TP32);
-    dma_tp32<D, NW>(buf + OFF_DOT, (const char*)p.dotp + tile * C::TP32);
-    if (w == NW - 1 && l < 16) {
-      const float* src = l < 8 ? p.lse + ((int64_t)b * p.Hq + h) * p.ncap + q0 + 4 * l
-                               : p.wsD + ((int64_t)b * p.Hq + h) * p.seg_len + (q0 - qs) + 4 * (l - 8);
-      dma16(src, buf + OFF_LD);
+    tplan.issue(buf + OFF_QT, (const char*)p.qtp + tile * C::TP32);
+    tplan.issue(buf + OFF_DOT, (const char*)p.dotp + tile * C::TP32);
+    if (l < LDC) {
+      const int64_t rowoff = ((int64_t)b * p.Hq + h) * p.seg_len + (q0 - qs);
+      const float* src = ld_chunk < 8 ? p.wsL2 + rowoff + 4 * ld_chunk : p.wsD + rowoff + 4 * (ld_chunk - 8);
+      dma16(src, buf + OFF_LD + 16 * LDC * w);
     }
   };
 
@@ -425,27 +435,12 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
     const float* lsel = (const float*)(buf + OFF_LD);
     const float* Dl = lsel + 32;
     f32x16 sacc = zero16(), pacc = zero16();
-    {
-      bf16x8 aq = ld_nat<D>(Ql, lc, hl), ad = ld_nat<D>(dOl, lc, hl), bk = ld_nat<D>(Kw, lc, hl);
 #pragma unroll
-      for (int s = 0; s < C::NS; ++s) {
-        bf16x8 aqn = aq, adn = ad, bkn = bk;
-        if (s + 1 < C::NS) {
-          aqn = ld_nat<D>(Ql, lc, 2 * (s + 1) + hl);
-          adn = ld_nat<D>(dOl, lc, 2 * (s + 1) + hl);
-          bkn = ld_nat<D>(Kw, lc, 2 * (s + 1) + hl);
-        }
-        sacc = Mfma<bf16>::mma(aq, bk, sacc);
-        pacc = Mfma<bf16>::mma(ad, vf[s], pacc);
-        aq = aqn;
-        ad = adn;
-        bk = bkn;
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int s = 0; s < C::NS; ++s) {
+      sacc = Mfma<bf16>::mma(ldo(Ql, rp.nat[s]), ldo(Kw, rp.nat[s]), sacc);
+      pacc = Mfma<bf16>::mma(ldo(dOl, rp.nat[s]), vf[s], pacc);
     }
     // lane = key kw0 + lc; register r = query q0 + 8(r/4) + 4hl + r%4
-    const bool need_mask = q0 < kw0 + 31;
-    const int kr = kw0 + lc;
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const f32x4 lq = *(const f32x4*)(lsel + 8 * rg + 4 * hl);
@@ -453,33 +448,27 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * rg + i;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.scale_log2, -lq[i] * kLog2e));
-        if (need_mask && q0 + 8 * rg + 4 * hl + i < kr) pv = 0.f;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.scale_log2, -lq[i]));
         sacc[r] = pv;
         pacc[r] = pv * (pacc[r] - dd[i]);
       }
     }
-    {
-      bf16x8 pf = frag_from_acc(sacc, 0), sf = frag_from_acc(pacc, 0);
-      bf16x8 bdo = ld_tp(dOTl, lc, hl), bq = ld_tp(QTl, lc, hl);
+    if (q0 < kw0 + 31) {                                          // diagonal step: causal mask
+      const int kr = kw0 + lc;
 #pragma unroll
-      for (int idx = 0; idx < 2 * C::NDB; ++idx) {
-        const int db = idx % C::NDB;
-        const int jn = (idx + 1) / C::NDB, dbn = (idx + 1) % C::NDB;
-        bf16x8 bdon = bdo, bqn = bq;
-        if (idx + 1 < 2 * C::NDB) {
-          bdon = ld_tp(dOTl, dbn * 32 + lc, 2 * jn + hl);
-          bqn = ld_tp(QTl, dbn * 32 + lc, 2 * jn + hl);
+      for (int r = 0; r < 16; ++r)
+        if (q0 + 8 * (r >> 2) + 4 * hl + (r & 3) < kr) {
+          sacc[r] = 0.f;
+          pacc[r] = 0.f;
         }
-        if (idx == C::NDB) {
-          pf = frag_from_acc(sacc, 1);
-          sf = frag_from_acc(pacc, 1);
-        }
-        dv[db] = Mfma<bf16>::mma(pf, bdo, dv[db]);
-        dk[db] = Mfma<bf16>::mma(sf, bq, dk[db]);
-        bdo = bdon;
-        bq = bqn;
-        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bf16x8 pf = frag_from_acc(sacc, j), sf = frag_from_acc(pacc, j);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        dv[db] = Mfma<bf16>::mma(pf, ldo(dOTl + db * 2048, rp.tp[j]), dv[db]);
+        dk[db] = Mfma<bf16>::mma(sf, ldo(QTl + db * 2048, rp.tp[j]), dk[db]);
       }
     }
   };
@@ -539,8 +528,11 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
   using C = T64<D>;
   constexpr int OFF_K = 0, OFF_V = C::NAT32, OFF_KT = 2 * C::NAT32;
   constexpr int STAGE = 2 * C::NAT32 + C::TP32;
+  using DC = DmaCount<D, NW>;
+  constexpr int PER = 2 * DC::NAT_W + DC::TP_W;  // direct-to-LDS instructions per wave per step
   __shared__ __attribute__((aligned(1024))) char sA[STAGE];
   __shared__ __attribute__((aligned(1024))) char sB[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sC[STAGE];
   __shared__ int ktab[kKeptTab];
 
   const int b = blockIdx.z, h = blockIdx.y;
@@ -575,7 +567,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
         qf[qb][s] = *(const bf16x8*)(qrow + (16 * s + 8 * hl) * 2);
         df[qb][s] = *(const bf16x8*)(drow + (16 * s + 8 * hl) * 2);
       }
-      lse2[qb] = p.lse[((int64_t)b * p.Hq + h) * p.ncap + qr] * kLog2e;
+      lse2[qb] = p.wsL2[((int64_t)b * p.Hq + h) * p.seg_len + (qr - qs)];
       Dv[qb] = p.wsD[((int64_t)b * p.Hq + h) * p.seg_len + (qr - qs)];
     }
   }
@@ -589,12 +581,19 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
   const char* vbase = (const char*)((const bf16*)p.v + b * p.vs[0] + g * p.vs[2]);
   const int64_t kstride = p.ks[1] * 2, vstride = p.vs[1] * 2;
   const char* ktp = (const char*)p.ktp + (((int64_t)b * p.Hkv + g) * (p.ncap / 32)) * C::TP32;
+  NatPlan<D, NW> kplan, vplan;
+  kplan.init(kstride);
+  vplan.init(vstride);
+  TpPlan<D, NW> tplan;
+  tplan.init();
+  ReadPlan<D> rp;
+  rp.init();
 
   auto issue = [&](int step, char* buf) {
     const int pos0 = kt.pos(step * 32);
-    dma_nat32<D, NW>(buf + OFF_K, kbase + (int64_t)pos0 * kstride, kstride);
-    dma_nat32<D, NW>(buf + OFF_V, vbase + (int64_t)pos0 * vstride, vstride);
-    dma_tp32<D, NW>(buf + OFF_KT, ktp + (int64_t)step * C::TP32);
+    kplan.issue(buf + OFF_K, kbase + (int64_t)pos0 * kstride);
+    vplan.issue(buf + OFF_V, vbase + (int64_t)pos0 * vstride);
+    tplan.issue(buf + OFF_KT, ktp + (int64_t)step * C::TP32);
   };
 
   auto compute = [&](int step, const char* buf) {
@@ -609,71 +608,58 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
       st[qb] = zero16();
       dp[qb] = zero16();
     }
-    {
-      bf16x8 ak = ld_nat<D>(Kl, lc, hl), av = ld_nat<D>(Vl, lc, hl);
 #pragma unroll
-      for (int s = 0; s < C::NS; ++s) {
-        bf16x8 akn = ak, avn = av;
-        if (s + 1 < C::NS) {
-          akn = ld_nat<D>(Kl, lc, 2 * (s + 1) + hl);
-          avn = ld_nat<D>(Vl, lc, 2 * (s + 1) + hl);
-        }
+    for (int s = 0; s < C::NS; ++s) {
+      const bf16x8 ak = ldo(Kl, rp.nat[s]), av = ldo(Vl, rp.nat[s]);
 #pragma unroll
-        for (int qb = 0; qb < NB; ++qb) {
-          st[qb] = Mfma<bf16>::mma(ak, qf[qb][s], st[qb]);
-          dp[qb] = Mfma<bf16>::mma(av, df[qb][s], dp[qb]);
-        }
-        ak = akn;
-        av = avn;
-        if (NB > 1) __builtin_amdgcn_sched_barrier(0);
+      for (int qb = 0; qb < NB; ++qb) {
+        st[qb] = Mfma<bf16>::mma(ak, qf[qb][s], st[qb]);
+        dp[qb] = Mfma<bf16>::mma(av, df[qb][s], dp[qb]);
       }
     }
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      const int qr = qw0 + 32 * qb + lc;
-      const bool need_mask = kr0 + 31 > qw0 + 32 * qb;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qb][r], p.scale_log2, -lse2[qb]));
-        if (need_mask && kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) > qr) pv = 0.f;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qb][r], p.scale_log2, -lse2[qb]));
         st[qb][r] = pv * (dp[qb][r] - Dv[qb]);
       }
+      if (kr0 + 31 > qw0 + 32 * qb) {                            // diagonal step: causal mask
+        const int qr = qw0 + 32 * qb + lc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) > qr) st[qb][r] = 0.f;
+      }
     }
-    {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
       bf16x8 af[NB];
 #pragma unroll
-      for (int qb = 0; qb < NB; ++qb) af[qb] = frag_from_acc(st[qb], 0);
-      bf16x8 bk = ld_tp(KTl, lc, hl);
+      for (int qb = 0; qb < NB; ++qb) af[qb] = frag_from_acc(st[qb], j);
 #pragma unroll
-      for (int idx = 0; idx < 2 * C::NDB; ++idx) {
-        const int db = idx % C::NDB;
-        const int jn = (idx + 1) / C::NDB, dbn = (idx + 1) % C::NDB;
-        const bf16x8 bkn = idx + 1 < 2 * C::NDB ? ld_tp(KTl, dbn * 32 + lc, 2 * jn + hl) : bk;
-        if (idx == C::NDB) {
-#pragma unroll
-          for (int qb = 0; qb < NB; ++qb) af[qb] = frag_from_acc(st[qb], 1);
-        }
+      for (int db = 0; db < C::NDB; ++db) {
+        const bf16x8 bk = ldo(KTl + db * 2048, rp.tp[j]);
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb) acc[qb][db] = Mfma<bf16>::mma(af[qb], bk, acc[qb][db]);
-        bk = bkn;
-        if (NB > 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
+  auto stage = [&](int t, const char* cur, char* nxt) {
+    if (!DC::EXACT || t + 1 >= nsteps) wait_all_mem();
+    else wait_vm<PER>();
+    __syncthreads();
+    if (t + 2 < nsteps) issue(t + 2, nxt);
+    compute(t, cur);
+  };
   issue(0, sA);
-  wait_all_mem();
-  __syncthreads();
-  for (int step = 0; step < nsteps; step += 2) {
-    if (step + 1 < nsteps) issue(step + 1, sB);
-    compute(step, sA);
-    wait_all_mem();
-    __syncthreads();
-    if (step + 1 >= nsteps) break;
-    if (step + 2 < nsteps) issue(step + 2, sA);
-    compute(step + 1, sB);
-    wait_all_mem();
-    __syncthreads();
+  if (nsteps > 1) issue(1, sB);
+  for (int t = 0; t < nsteps; t += 3) {
+    stage(t, sA, sC);
+    if (t + 1 >= nsteps) break;
+    stage(t + 1, sB, sA);
+    if (t + 2 >= nsteps) break;
+    stage(t + 2, sC, sB);
   }
 
   if (!active) return;

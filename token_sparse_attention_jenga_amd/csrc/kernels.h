@@ -55,6 +55,7 @@ struct BwdParams {
   float* dk;
   float* dv;
   float* wsD;    // [B][Hq][L]   dot(dO, O) of the segment's queries
+  float* wsL2;   // bf16 path: [B][Hq][L] lse of the segment's queries in the log2 domain
   void* wsdO;    // [B][L][Hq][D] dOut rows of the segment in operand dtype, by kept rank
   void* ktp;     // bf16 path: [B][Hkv][ncap/32] TP tiles of the kept K rows
   void* qtp;     // bf16 path: [B][Hq][L/32] TP tiles of the segment's Q rows

@@ -2,10 +2,13 @@
 //
 // Two LDS tile forms, both filled with gfx950 direct-to-LDS loads (global_load_lds_dwordx4:
 // lane i of a wave writes its 16 bytes at LDS base + 16*i, from any global address):
-//   natural tile  [32 rows][D] bf16, 16-byte chunk c of row r stored at chunk c ^ (r & 7);
-//                 read as MFMA operands whose reduction runs along head_dim.
+//   natural tile  [32 rows][D] bf16, 16-byte chunk c of row r stored at chunk c ^ (r % CPR)
+//                 (CPR = chunks per row); read as MFMA operands whose reduction runs along
+//                 head_dim.
 //   TP tile       [D][32 positions] bf16: row r of the source tile sits at position pi(r),
-//                 pi swapping bits 2 and 3 of r.  Chunk c of line d stored at c ^ ((d>>2)&3).
+//                 pi swapping bits 2 and 3 of r.  Chunk c of line d stored at c ^ tpswz(d).
+// Both swizzles make every 16-lane (and every 8-lane) group of a 16-byte read hit distinct
+// banks for the access patterns below.
 //                 One 16-byte read at line d, chunk 2j + h gives the 8 source rows that lane
 //                 half h needs for k-step j when the other operand comes straight from a
 //                 32x32 accumulator (registers 8j..8j+7 hold rows 16j + pi(8h + i)).
@@ -36,6 +39,23 @@ __device__ inline void dma16(const void* g, char* lds) {
 // Wait for every outstanding memory operation of this wave (direct-to-LDS loads included).
 __device__ inline void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until at most N vector-memory operations of this wave are outstanding (they complete in
+// issue order), leaving the newest N -- later pipeline stages -- in flight.
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Direct-to-LDS instructions one wave issues for a tile (uniform across waves iff exact).
+template <int D, int NW>
+struct DmaCount {
+  static constexpr int NAT = 32 * T64<D>::CPR / 64;
+  static constexpr int TP = D * 64 / 1024;
+  static constexpr bool EXACT = NAT % NW == 0 && TP % NW == 0;
+  static constexpr int NAT_W = NAT / NW, TP_W = TP / NW;
+};
+
 // Natural 32-row tile: rows at g_row0 + r * row_stride (bytes).  NW waves share the copy.
 template <int D, int NW>
 __device__ inline void dma_nat32(char* lds_tile, const char* g_row0, int64_t row_stride) {
@@ -46,10 +66,12 @@ __device__ inline void dma_nat32(char* lds_tile, const char* g_row0, int64_t row
   for (int n = w; n < NI; n += NW) {
     const int idx = n * 64 + l;
     const int row = idx / CPR, phys = idx % CPR;
-    const int c = phys ^ (row & 7);
+    const int c = phys ^ (row & (CPR - 1));
     dma16(g_row0 + row * row_stride + c * 16, lds_tile + n * 1024);
   }
 }
+
+__device__ inline int tpswz(int d) { return ((d >> 1) & 3) ^ ((d >> 3) & 1); }
 
 // TP tile: a contiguous [D][32] bf16 block in global memory.
 template <int D, int NW>
@@ -60,24 +82,90 @@ __device__ inline void dma_tp32(char* lds_tile, const char* g_tile) {
   for (int n = w; n < NI; n += NW) {
     const int idx = n * 64 + l;
     const int d = idx >> 2, phys = idx & 3;
-    const int c = phys ^ ((d >> 2) & 3);
+    const int c = phys ^ tpswz(d);
     dma16(g_tile + d * 64 + c * 16, lds_tile + n * 1024);
   }
 }
 
+// Per-lane address offsets of one wave's direct-to-LDS instructions, computed once per kernel
+// so that a step only adds its (wave-uniform) base address.
+template <int D, int NW>
+struct NatPlan {
+  static constexpr int NI = DmaCount<D, NW>::NAT;
+  static constexpr int MAXW = (NI + NW - 1) / NW;
+  int off[MAXW];
+  __device__ void init(int64_t row_stride) {
+    constexpr int CPR = T64<D>::CPR;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < MAXW; ++i) {
+      const int idx = (w + i * NW) * 64 + l;
+      const int row = idx / CPR, phys = idx % CPR;
+      off[i] = (int)(row * row_stride) + ((phys ^ (row & (CPR - 1))) << 4);
+    }
+  }
+  __device__ void issue(char* lds_tile, const char* g_row0) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < MAXW; ++i)
+      if (w + i * NW < NI) dma16(g_row0 + off[i], lds_tile + (w + i * NW) * 1024);
+  }
+};
+
+template <int D, int NW>
+struct TpPlan {
+  static constexpr int NI = DmaCount<D, NW>::TP;
+  static constexpr int MAXW = (NI + NW - 1) / NW;
+  int off[MAXW];
+  __device__ void init() {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < MAXW; ++i) {
+      const int idx = (w + i * NW) * 64 + l;
+      const int d = idx >> 2, phys = idx & 3;
+      off[i] = d * 64 + ((phys ^ tpswz(d)) << 4);
+    }
+  }
+  __device__ void issue(char* lds_tile, const char* g_tile) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < MAXW; ++i)
+      if (w + i * NW < NI) dma16(g_tile + off[i], lds_tile + (w + i * NW) * 1024);
+  }
+};
+
+// Per-lane LDS read offsets for the MFMA operands of a wave whose rows are its lane index:
+// natural tile, k-step s:  row lc, chunk 2s + hl;   TP tile, 32-wide block db, k-step j:
+// line db*32 + lc, chunk 2j + hl (the db part is a constant 2048*db).
+template <int D>
+struct ReadPlan {
+  int nat[T64<D>::NS];
+  int tp[2];
+  __device__ void init() {
+    const int l = threadIdx.x & 63, hl = l >> 5, lc = l & 31;
+    constexpr int CPR = T64<D>::CPR;
+#pragma unroll
+    for (int s = 0; s < T64<D>::NS; ++s) nat[s] = lc * T64<D>::ROWB + (((2 * s + hl) ^ (lc & (CPR - 1))) << 4);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) tp[j] = lc * 64 + (((2 * j + hl) ^ tpswz(lc)) << 4);
+  }
+};
+
+__device__ inline bf16x8 ldo(const char* tile, int off) { return *(const bf16x8*)(tile + off); }
+
 template <int D>
 __device__ inline bf16x8 ld_nat(const char* tile, int row, int c) {
-  return *(const bf16x8*)(tile + row * T64<D>::ROWB + ((c ^ (row & 7)) << 4));
+  return *(const bf16x8*)(tile + row * T64<D>::ROWB + ((c ^ (row & (T64<D>::CPR - 1))) << 4));
 }
 
 __device__ inline bf16x8 ld_tp(const char* tile, int d, int c) {
-  return *(const bf16x8*)(tile + d * 64 + ((c ^ ((d >> 2) & 3)) << 4));
+  return *(const bf16x8*)(tile + d * 64 + ((c ^ tpswz(d)) << 4));
 }
 
 // Kept-block table staged in LDS once per workgroup, so the hot loops resolve a kept rank to
 // its token position without a global-memory round trip.  Blocks beyond the table's capacity
 // fall back to the global list.
-constexpr int kKeptTab = 2048;
+constexpr int kKeptTab = 1024;
 
 struct KeptTab {
   const int* s;            // LDS copy of kept[0 .. min(n, kKeptTab))
