@@ -70,7 +70,10 @@ hipError_t launch_select(const SelectParams& p, hipStream_t st);
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, hipStream_t st);
 hipError_t launch_bwd_segment(const BwdParams& p, int dtype, int D, hipStream_t st);
 
-// bf16 kernels with 64 rows per wave (attn64.hip)
+// bf16 scoring with async LDS staging (score64.hip)
+hipError_t launch_score64(const ScoreParams& p, int D, hipStream_t st);
+
+// bf16 attention kernels (attn64.hip)
 hipError_t launch_fwd64(const FwdParams& p, int D, hipStream_t st);
 hipError_t launch_bwd64_pack_keys(const BwdParams& p, int D, hipStream_t st);
 hipError_t launch_bwd64_segment(const BwdParams& p, int D, hipStream_t st);

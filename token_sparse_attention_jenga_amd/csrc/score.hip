@@ -245,7 +245,13 @@ static hipError_t launch_score_t(const ScoreParams& p, hipStream_t st) {
 }
 
 hipError_t launch_score(const ScoreParams& p, int dtype, int D, hipStream_t st) {
-  if (dtype == 1) return D == 64 ? launch_score_t<bf16, 64>(p, st) : launch_score_t<bf16, 128>(p, st);
+  if (dtype == 1) {                      // bf16: async-staged kernels of score64.hip
+    hipError_t e = launch_score64(p, D, st);
+    if (e != hipSuccess) return e;
+    const int nkb = p.S / p.block;
+    k_score_reduce<<<dim3((nkb + 255) / 256, p.B), 256, 0, st>>>(p);
+    return hipGetLastError();
+  }
   return launch_score_t<float, 64>(p, st);    // fp32 operands: head_dim 64 only
 }
 
