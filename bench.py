@@ -28,6 +28,8 @@ if ROOT not in sys.path:
 
 BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 bf16 flop/clk/CU x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
+KERNELS = ("k_slse64", "k_smass64", "k_select", "k_pack_tp", "k_fwd64", "k_prep64", "k_dkdv32",
+           "k_dq64")
 METRIC = "fwd+bwd token-sparse attn TFLOP/s (kept FLOPs) & tokens/s at S=32K; % MFMA peak"
 
 
@@ -41,8 +43,12 @@ def parse():
                     help="attention over the selected blocks, or over a seeded scattered set")
     ap.add_argument("--segments", type=int, default=0, help="override backward segment count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_LOG"),
+                    help="no GPU work: turn rocprofv3 csv output of this bench (kernel trace, then "
+                         "FETCH_SIZE and WRITE_SIZE passes run with --copy-calibration) into the "
+                         "summaries kept under profiles/")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -56,8 +62,89 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def _short(name: str) -> str:
+    for k in KERNELS + ("k_score_reduce",):
+        if f"::{k}<" in name or f"::{k}(" in name:
+            return k
+    if "neg_kernel" in name:
+        return "calibration copy (elementwise neg, 1 GiB)"
+    return name.split("(")[0][:70]
+
+
+def summarize(trace_dir, fetch_dir, write_dir, bench_log, cfg_name="c5"):
+    """Write profiles/kernels_<cfg>.md (rocprofv3 kernel-trace stats next to the bench's own
+    HIP-event averages) and profiles/traffic_k_dkdv32_<cfg>.json (HBM bytes per launch from
+    FETCH_SIZE / WRITE_SIZE, each scaled by the ratio known bytes / counter of the calibration
+    copy, which moves exactly 1 GiB each way)."""
+    import csv
+    with open(bench_log) as f:
+        line = [x for x in f if x.startswith("{")][-1]
+    bench = json.loads(line)
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+
+    def counters(d):
+        agg = {}
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            k = _short(r["Kernel_Name"])
+            n, t = agg.get(k, (0, 0.0))
+            agg[k] = (n + 1, t + float(r["Counter_Value"]) * 1024.0)
+        return agg
+    fetch, write = counters(fetch_dir), counters(write_dir)
+    cal = "calibration copy (elementwise neg, 1 GiB)"
+    f_fac = 2**30 / (fetch[cal][1] / fetch[cal][0])
+    w_fac = 2**30 / (write[cal][1] / write[cal][0])
+    lines = [f"# Kernel times, {cfg_name} bench step (rocprofv3 kernel trace)", "",
+             "Command (repository root on the GPU host):", "",
+             "    cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+             "-d <repo>/gpurun_out/prof_trace -o run -- python3 <repo>/bench.py --steps 2 --warmup 1 "
+             "--no-cpu-baseline", "",
+             f"Kernel source hash {kernel_source_hash()}.  Columns: rocprofv3 calls / average / total "
+             "over warmup + timed steps; the bench's own HIP-event average over the timed steps.", "",
+             "| kernel | calls | rocprof avg us | rocprof total ms | % | bench event avg us |",
+             "|---|---|---|---|---|---|"]
+    ev = bench.get("kernel_avg_us", {})
+    for r in rows:
+        k = _short(r["Name"])
+        e = ev.get(k, {}).get("avg_us", "")
+        lines.append(f"| {k} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.2f} | {e} |")
+    lines += ["", "HBM counters (separate rocprofv3 --pmc runs of the same bench with --copy-calibration, "
+              "--steps 1 --warmup 1):", "",
+              "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/prof_fetch -o run -- "
+              "python3 <repo>/bench.py --steps 1 --warmup 1 --no-cpu-baseline --copy-calibration",
+              "    rocprofv3 --pmc WRITE_SIZE ... (same, -d <repo>/gpurun_out/prof_write)", "",
+              f"Calibration: the 1 GiB copy reads FETCH_SIZE {fetch[cal][1] / fetch[cal][0] / 2**20:.1f} MiB and "
+              f"WRITE_SIZE {write[cal][1] / write[cal][0] / 2**20:.1f} MiB, so counter bytes are scaled by "
+              f"{f_fac:.3f} (fetch) and {w_fac:.3f} (write).", "",
+              "| kernel | dispatches | fetch MiB/dispatch (scaled) | write MiB/dispatch (scaled) |",
+              "|---|---|---|---|"]
+    for k in sorted(fetch):
+        if k == cal or k not in write:
+            continue
+        n = fetch[k][0]
+        lines.append(f"| {k} | {n} | {fetch[k][1] / n * f_fac / 2**20:.1f} | "
+                     f"{write[k][1] / write[k][0] * w_fac / 2**20:.1f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"kernels_{cfg_name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    k = "k_dkdv32"
+    t = {"kernel": k, "config": cfg_name, "kernel_source_hash": kernel_source_hash(),
+         "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4),
+         "fetch_bytes_per_launch": round(fetch[k][1] / fetch[k][0] * f_fac),
+         "write_bytes_per_launch": round(write[k][1] / write[k][0] * w_fac)}
+    t["hbm_bytes_per_launch"] = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
+    with open(os.path.join(ROOT, "profiles", f"traffic_{k}_{cfg_name}.json"), "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    print("\n".join(lines))
+    print(json.dumps(t))
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(*args.summarize, cfg_name=args.config)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the token-sparse attention path here is single-GPU "
@@ -166,10 +253,12 @@ def main():
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    J.timing_enable(True)
     start.record(stream)
     for i in range(K):
         run_step(evs[i])
     end.record(stream)
+    J.timing_enable(False)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / K
@@ -190,31 +279,44 @@ def main():
     tflops = (fwd_flop + bwd_flop) / (attn_ms * 1e-3) / 1e12
     score_flop = 2 * 2.0 * D * Hq * B * L * S * (S + 1) / 2
 
-    # dominant kernel of the step: the backward main kernel (one call = N segments of
-    # prep + main, all on this stream); roofline against the bf16 MFMA peak
-    bwd_call_ms = phase["bwd"] / L
-    bwd_flop_call = bwd_flop / L
-    achieved = bwd_flop_call / (bwd_call_ms * 1e-3) / 1e12
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "traffic_k_bwd_main_c5.json")
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            tj = json.load(f)
-        if tj.get("kernel_source_hash") == kernel_source_hash() and tj.get("config") == cfg.name:
-            traffic = tj.get("bytes_per_call")
-    roofline = {"kernel": "attention backward call (k_dkdv64 + k_dq64 + prologue/pack), %d segments" % nseg,
-                "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                "algorithmic_flop_per_call": bwd_flop_call, "avg_call_ms": round(bwd_call_ms, 4)}
+    # dominant attention kernel: k_dkdv32 (the dK/dV half of the backward), timed by the
+    # library's own HIP events on the stream it runs on, over the timed steps above.  Its
+    # algorithmic work is four 2*D contractions per (query head, causal kept pair): the score
+    # recompute, dP, dV and dK.
+    kern_ms = {}
+    for name in KERNELS:
+        n, t = J.timing_query(name)
+        if n:
+            kern_ms[name] = (n, t)
+    n_dkdv, t_dkdv = kern_ms.get("k_dkdv32", (0, 0.0))
+    roofline = None
+    if n_dkdv:
+        dkdv_flop_launch = 8.0 * D * Hq * pairs * K / n_dkdv
+        avg_ms = t_dkdv / n_dkdv
+        achieved = dkdv_flop_launch / (avg_ms * 1e-3) / 1e12
+        traffic = None
+        tfile = os.path.join(ROOT, "profiles", f"traffic_k_dkdv32_{cfg.name}.json")
+        if os.path.exists(tfile) and args.kept == "selected" and nseg == cfg.n_segments:
+            with open(tfile) as f:
+                tj = json.load(f)
+            if tj.get("kernel_source_hash") == kernel_source_hash():
+                traffic = tj.get("hbm_bytes_per_launch")
+        roofline = {"kernel": "k_dkdv32", "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                    "algorithmic_flop_per_launch": dkdv_flop_launch, "launches": n_dkdv,
+                    "avg_launch_us": round(avg_ms * 1e3, 2)}
+    kernel_avg_us = {kk: {"launches": n, "avg_us": round(1e3 * t / n, 2)} for kk, (n, t) in kern_ms.items()}
 
     copy_ms = None
     if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # plain elementwise copy (16-byte vector loads/stores), 1 GiB read + 1 GiB written
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         bcopy = torch.empty_like(a)
         torch.cuda.synchronize()
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record(stream)
-        bcopy.copy_(a)
+        torch.neg(a, out=bcopy)
         c1.record(stream)
         torch.cuda.synchronize()
         copy_ms = c0.elapsed_time(c1)
@@ -258,12 +360,15 @@ def main():
         "score_tflops_algorithmic": round(score_flop / (phase["score"] * 1e-3) / 1e12, 2),
         "kept_tokens_per_layer": nks,
         "roofline": roofline,
+        "kernel_avg_us": kernel_avg_us,
         "cpu_baseline": cpu,
         "memory": mem,
         "input_gen_s": round(gen_s, 1),
     }
     if copy_ms is not None:
-        out["copy_1gib_ms"] = round(copy_ms, 4)
+        out["copy_calibration"] = {"kernel": "elementwise neg, float32, 1 GiB in + 1 GiB out",
+                                   "ms": round(copy_ms, 4),
+                                   "gbs": round(2 * 2**30 / (copy_ms * 1e-3) / 1e9, 1)}
     print(json.dumps(out), flush=True)
 
 

@@ -171,7 +171,8 @@ int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, 
  *   dk, dv            [B][S][Hkv][D] fp32, dense, accumulated (+=) at kept rows only
  *   n_segments        1 <= n_segments <= max_kept_blocks*block/64
  *   workspace         >= jenga_workspace_bytes(p, JENGA_OP_BWD, max_kept_blocks, n_segments)
- * dq receives fp32 atomic additions, so its low bits may differ run to run.
+ * bf16: every gradient is accumulated by a fixed schedule, so results repeat bit for bit.
+ * fp32: dq receives fp32 atomic additions, so its low bits may differ run to run.
  */
 int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const void* k,
                                     const void* v, const int32_t* kept_idx, const int32_t* n_kept,
@@ -179,6 +180,23 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
                                     const float* dout, float* dq, float* dk, float* dv,
                                     int n_segments, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * Kernel timing (instrumentation; not part of the method).
+ *
+ * jenga_timing_enable(1) discards earlier records and, from then on, brackets every kernel
+ * launched by the entry points above with two HIP events recorded on that call's stream;
+ * jenga_timing_enable(0) stops recording (the records stay readable).  Kernel names:
+ * k_slse64, k_smass64 (bf16 scoring), k_select, k_pack_tp, k_fwd64, k_prep64, k_dkdv32,
+ * k_dq64 (bf16 attention).  The fp32 kernels are not bracketed.
+ *
+ * jenga_timing_query(kernel, launches, total_ms) waits for the recorded events of that name
+ * and returns how many launches were recorded and the sum of their event-to-event times.
+ * Errors: INVALID_ARG for a null pointer or enable not in {0, 1}; LAUNCH if an event query
+ * fails.  Not thread-safe; one process-wide record list.
+ */
+int jenga_timing_enable(int enable);
+int jenga_timing_query(const char* kernel, int32_t* launches, double* total_ms);
 
 #ifdef __cplusplus
 }

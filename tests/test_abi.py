@@ -134,3 +134,12 @@ def test_workspace_scales_with_segments_and_kept_blocks(J):
     assert abs(w8_half * 2 - w8) <= 4096          # everything scales with the kept tokens
     assert J.workspace_bytes(p, J.JENGA_OP_FWD, 128) == ktp
     assert J.workspace_bytes(_problem(J), J.JENGA_OP_FWD, 8) == 0       # fp32 path needs none
+
+
+def test_timing_calls_without_gpu_work(J):
+    assert J.lib.jenga_timing_enable(2) == J.JENGA_ERR_INVALID_ARG
+    J.timing_enable(True)
+    assert J.timing_query("k_dkdv32") == (0, 0.0)          # nothing launched yet
+    J.timing_enable(False)
+    n = ctypes.c_int32(0)
+    assert J.lib.jenga_timing_query(None, ctypes.byref(n), None) == J.JENGA_ERR_INVALID_ARG

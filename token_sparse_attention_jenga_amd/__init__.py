@@ -30,7 +30,7 @@ JENGA_OP_BWD = 2
 
 EXPORTED = ["jenga_status_string", "jenga_topk_count", "jenga_workspace_bytes",
             "jenga_score_blocks", "jenga_select_blocks", "jenga_sparse_attn_fwd",
-            "jenga_sparse_attn_bwd_segmented"]
+            "jenga_sparse_attn_bwd_segmented", "jenga_timing_enable", "jenga_timing_query"]
 
 
 class JengaProblem(ctypes.Structure):
@@ -70,6 +70,11 @@ def _load() -> ctypes.CDLL:
     lib.jenga_sparse_attn_bwd_segmented.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                                                     vp, i32, vp, sz, vp]
     lib.jenga_sparse_attn_bwd_segmented.restype = i32
+    lib.jenga_timing_enable.argtypes = [i32]
+    lib.jenga_timing_enable.restype = i32
+    lib.jenga_timing_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.POINTER(ctypes.c_double)]
+    lib.jenga_timing_query.restype = i32
     return lib
 
 
@@ -82,6 +87,22 @@ def status_string(status: int) -> str:
 
 def topk_count(keep_ratio: float, n_blocks: int) -> int:
     return int(lib.jenga_topk_count(ctypes.c_float(keep_ratio), int(n_blocks)))
+
+
+def timing_enable(enable: bool) -> None:
+    """Start (clearing earlier records) or stop per-kernel HIP-event timing in the library."""
+    st = lib.jenga_timing_enable(1 if enable else 0)
+    if st != JENGA_OK:
+        raise JengaError("jenga_timing_enable", st)
+
+
+def timing_query(kernel: str):
+    """(launches, total_ms) recorded for one kernel name since the last timing_enable(True)."""
+    n, t = ctypes.c_int32(0), ctypes.c_double(0.0)
+    st = lib.jenga_timing_query(kernel.encode(), ctypes.byref(n), ctypes.byref(t))
+    if st != JENGA_OK:
+        raise JengaError("jenga_timing_query", st)
+    return int(n.value), float(t.value)
 
 
 # ------------------------------------------------------------------------------------------

@@ -302,4 +302,20 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
   return JENGA_OK;
 }
 
+int jenga_timing_enable(int enable) {
+  if (enable != 0 && enable != 1) return JENGA_ERR_INVALID_ARG;
+  jenga::timing_set(enable == 1);
+  return JENGA_OK;
+}
+
+int jenga_timing_query(const char* kernel, int32_t* launches, double* total_ms) {
+  if (!kernel || !launches || !total_ms) return JENGA_ERR_INVALID_ARG;
+  int n = 0;
+  double t = 0.0;
+  if (jenga::timing_query(kernel, &n, &t) != hipSuccess) return JENGA_ERR_LAUNCH;
+  *launches = n;
+  *total_ms = t;
+  return JENGA_OK;
+}
+
 }  // extern "C"

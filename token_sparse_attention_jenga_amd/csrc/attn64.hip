@@ -75,6 +75,7 @@ template <int D>
 static hipError_t pack_tp(const PackArgs& a, int B, hipStream_t st) {
   const int ntiles = (a.rank_count + 31) / 32;
   if (ntiles <= 0) return hipSuccess;
+  TimedLaunch tl("k_pack_tp", st);
   k_pack_tp<D><<<dim3(ntiles, a.H, B), 256, 0, st>>>(a);
   return hipGetLastError();
 }
@@ -698,6 +699,7 @@ static hipError_t launch_fwd64_t(const FwdParams& p, hipStream_t st) {
   hipError_t e = pack_tp<D>(a, p.B, st);
   if (e != hipSuccess) return e;
   constexpr int RG = 32 * FWD_NB * FWD_NW;
+  TimedLaunch tl("k_fwd64", st);
   k_fwd64<D, FWD_NB, FWD_NW><<<dim3((p.ncap + RG - 1) / RG, p.Hq, p.B), 64 * FWD_NW, 0, st>>>(p);
   return hipGetLastError();
 }
@@ -722,8 +724,12 @@ static hipError_t bwd64_segment_t(const BwdParams& p, hipStream_t st) {
   const int L = p.seg_len;
   const int seg_cap = min(L, p.ncap - p.seg * L);          // ranks of this segment (capacity)
   if (seg_cap <= 0) return hipSuccess;
-  k_prep64<D><<<dim3((seg_cap + 31) / 32, p.Hq, p.B), 256, 0, st>>>(p);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  {
+    TimedLaunch tl("k_prep64", st);
+    k_prep64<D><<<dim3((seg_cap + 31) / 32, p.Hq, p.B), 256, 0, st>>>(p);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   PackArgs a{p.q, p.qs[0], p.qs[1], p.qs[2], p.kept, p.n_kept, p.block, p.nkb, p.max_kept_blocks,
              p.seg * L, seg_cap, L / 32, p.Hq, p.qtp};
@@ -731,10 +737,14 @@ static hipError_t bwd64_segment_t(const BwdParams& p, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int seg_end = p.seg * L + seg_cap;
   constexpr int KG = 32 * DKDV_NW;
-  k_dkdv32<D, DKDV_NW><<<dim3((seg_end + KG - 1) / KG, p.Hkv, p.B), 64 * DKDV_NW, 0, st>>>(p);
-  e = hipGetLastError();
+  {
+    TimedLaunch tl("k_dkdv32", st);
+    k_dkdv32<D, DKDV_NW><<<dim3((seg_end + KG - 1) / KG, p.Hkv, p.B), 64 * DKDV_NW, 0, st>>>(p);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   constexpr int QG = 32 * DQ_NB * DQ_NW;
+  TimedLaunch tl("k_dq64", st);
   k_dq64<D, DQ_NB, DQ_NW><<<dim3((seg_cap + QG - 1) / QG, p.Hq, p.B), 64 * DQ_NW, 0, st>>>(p);
   return hipGetLastError();
 }

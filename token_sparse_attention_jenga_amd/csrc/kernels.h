@@ -73,6 +73,23 @@ hipError_t launch_bwd_segment(const BwdParams& p, int dtype, int D, hipStream_t 
 // bf16 scoring with async LDS staging (score64.hip)
 hipError_t launch_score64(const ScoreParams& p, int D, hipStream_t st);
 
+// Per-kernel event timing (timing.cpp).  A TimedLaunch placed around a launch records a start
+// event on construction and a stop event on destruction when timing is enabled.
+class TimedLaunch {
+ public:
+  TimedLaunch(const char* name, hipStream_t st);
+  ~TimedLaunch();
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
+
+ private:
+  hipStream_t st_;
+  long idx_;
+};
+bool timing_enabled();
+void timing_set(bool on);
+hipError_t timing_query(const char* name, int* launches, double* total_ms);
+
 // bf16 attention kernels (attn64.hip)
 hipError_t launch_fwd64(const FwdParams& p, int D, hipStream_t st);
 hipError_t launch_bwd64_pack_keys(const BwdParams& p, int D, hipStream_t st);

@@ -202,9 +202,14 @@ constexpr int SCORE_NW = 4;
 template <int D>
 static hipError_t launch_score64_t(const ScoreParams& p, hipStream_t st) {
   constexpr int RG = 32 * SCORE_NW;
-  k_slse64<D, SCORE_NW><<<dim3((p.S + RG - 1) / RG, p.Hq, p.B), 64 * SCORE_NW, 0, st>>>(p);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  {
+    TimedLaunch tl("k_slse64", st);
+    k_slse64<D, SCORE_NW><<<dim3((p.S + RG - 1) / RG, p.Hq, p.B), 64 * SCORE_NW, 0, st>>>(p);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
+  TimedLaunch tl("k_smass64", st);
   k_smass64<D, SCORE_NW><<<dim3((p.S + RG - 1) / RG, p.Hq, p.B), 64 * SCORE_NW, 0, st>>>(p);
   return hipGetLastError();
 }

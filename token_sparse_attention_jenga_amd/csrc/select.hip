@@ -85,6 +85,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectParams p) {
 }
 
 hipError_t launch_select(const SelectParams& p, hipStream_t st) {
+  TimedLaunch tl("k_select", st);
   k_select<<<p.B, kSelThreads, (size_t)p.nkb * sizeof(uint32_t), st>>>(p);
   return hipGetLastError();
 }
