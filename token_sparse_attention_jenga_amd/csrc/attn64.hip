@@ -101,14 +101,15 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
   __shared__ __attribute__((aligned(1024))) char sC[STAGE];
   __shared__ int ktab[kKeptTab];
 
-  const int b = blockIdx.z, h = blockIdx.y;
+  const Tile3 tl = xcd_tile();
+  const int b = tl.z, h = tl.y;
   const int g = h / (p.Hq / p.Hkv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
   const int32_t* kept = p.kept + (int64_t)b * p.nkb;
   const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
   const int nqt = (Nk + RG - 1) / RG;
-  if ((int)blockIdx.x >= nqt) return;
-  const int q0 = (nqt - 1 - (int)blockIdx.x) * RG;      // heaviest tiles first
+  if (tl.x >= nqt) return;
+  const int q0 = (nqt - 1 - tl.x) * RG;                  // heaviest tiles first
   const int qw0 = q0 + RW * w;
   const bool active = qw0 < Nk;                          // Nk is a multiple of 64 >= RW
   const int qlast = min(q0 + RG, Nk) - 1;
@@ -353,14 +354,15 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
   __shared__ __attribute__((aligned(1024))) char sB[STAGE];
   __shared__ int ktab[kKeptTab];
 
-  const int b = blockIdx.z, g = blockIdx.y;
+  const Tile3 tl = xcd_tile();
+  const int b = tl.z, g = tl.y;
   const int G = p.Hq / p.Hkv;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
   const int32_t* kept = p.kept + (int64_t)b * p.nkb;
   const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
   const int qs = p.seg * p.seg_len;
   const int qe = min(qs + p.seg_len, Nk);
-  const int k0 = blockIdx.x * KEYS;
+  const int k0 = tl.x * KEYS;
   if (qs >= qe || k0 >= qe) return;
   const int kw0 = k0 + 32 * w;
   const bool key_valid = kw0 < Nk;                               // Nk is a multiple of 64
@@ -536,7 +538,8 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
   __shared__ __attribute__((aligned(1024))) char sC[STAGE];
   __shared__ int ktab[kKeptTab];
 
-  const int b = blockIdx.z, h = blockIdx.y;
+  const Tile3 tl = xcd_tile();
+  const int b = tl.z, h = tl.y;
   const int g = h / (p.Hq / p.Hkv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
   const int32_t* kept = p.kept + (int64_t)b * p.nkb;
@@ -544,8 +547,8 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
   const int qs = p.seg * p.seg_len;
   const int qe = min(qs + p.seg_len, Nk);
   const int nqt = (qe - qs + RG - 1) / RG;
-  if (qs >= qe || (int)blockIdx.x >= nqt) return;
-  const int q0 = qs + (nqt - 1 - (int)blockIdx.x) * RG;         // heaviest tiles first
+  if (qs >= qe || tl.x >= nqt) return;
+  const int q0 = qs + (nqt - 1 - tl.x) * RG;                    // heaviest tiles first
   const int qw0 = q0 + RW * w;
   const bool active = qw0 < qe;                                  // qe - qs multiple of 64
   const int qlast = min(q0 + RG, qe) - 1;

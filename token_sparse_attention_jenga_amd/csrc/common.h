@@ -109,4 +109,21 @@ __device__ inline void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 
 __device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// XCD-aware workgroup numbering.  An MI355X has 8 XCDs, each with its own L2, and the
+// dispatcher hands workgroups, in linear launch order, to XCD (index % 8) in turn.  xcd_tile()
+// renumbers them so that XCD x runs one contiguous range of logical tiles (x fastest, then y,
+// then z) in launch order; the tiles of one (batch, head) then share one L2 instead of
+// streaming the same K/V or Q rows through all eight.  A bijection for any grid size.
+struct Tile3 {
+  int x, y, z;
+};
+__device__ inline Tile3 xcd_tile() {
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int nwg = nx * ny * (int)gridDim.z;
+  const int lin = (int)blockIdx.x + nx * ((int)blockIdx.y + ny * (int)blockIdx.z);
+  const int q = nwg >> 3, r = nwg & 7, xcd = lin & 7, slot = lin >> 3;
+  const int L = xcd * q + min(xcd, r) + slot;
+  return {L % nx, (L / nx) % ny, L / (nx * ny)};
+}
+
 }  // namespace jenga

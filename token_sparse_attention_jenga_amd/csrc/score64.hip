@@ -28,11 +28,12 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
   __shared__ __attribute__((aligned(1024))) char sB[C::NAT32];
   __shared__ __attribute__((aligned(1024))) char sC[C::NAT32];
 
-  const int b = blockIdx.z, h = blockIdx.y;
+  const Tile3 tl = xcd_tile();
+  const int b = tl.z, h = tl.y;
   const int g = h / (p.Hq / p.Hkv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
   const int nqt = (p.S + RG - 1) / RG;
-  const int q0 = (nqt - 1 - (int)blockIdx.x) * RG;      // heaviest tiles first
+  const int q0 = (nqt - 1 - tl.x) * RG;                  // heaviest tiles first
   const int qw0 = q0 + 32 * w;
   const bool active = qw0 < p.S;                         // S is a multiple of 64
   const int qi = qw0 + lc;
@@ -114,10 +115,11 @@ __global__ __launch_bounds__(64 * NW, 2) void k_smass64(ScoreParams p) {
   __shared__ __attribute__((aligned(1024))) char sB[STAGE];
   __shared__ __attribute__((aligned(1024))) char sC[STAGE];
 
-  const int b = blockIdx.z, h = blockIdx.y;
+  const Tile3 tl = xcd_tile();
+  const int b = tl.z, h = tl.y;
   const int g = h / (p.Hq / p.Hkv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
-  const int k0 = blockIdx.x * KG;
+  const int k0 = tl.x * KG;
   const int kw0 = k0 + 32 * w;
   const bool active = kw0 < p.S;
   const int kj = kw0 + lc;
