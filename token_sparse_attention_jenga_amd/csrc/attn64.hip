@@ -1,24 +1,19 @@
-// bf16 token-sparse attention forward and segmented backward for gfx950, 64 rows per wave.
+// bf16 token-sparse attention forward and segmented backward for gfx950.
 //
 // Jenga (papercache notes, §4.4): kept rows are addressed in place through the kept-block
 // list (permutation-free token movement), the forward adds its output into the residual in
 // place, and the backward runs segment by segment (segment-based peak cutting).
 //
-// Why 64 rows per wave: with 32 rows, every MFMA operand streamed from LDS feeds 32 rows,
-// i.e. one LDS byte per 32 MFMA flops -- about the measured LDS rate of a CU (~140 B/clk
-// against 4096 flop/clk).  With 64 rows the LDS traffic halves.  The price is register
-// space (two 32x32 accumulator blocks per GEMM), so these kernels run one wave per SIMD with
-// up to 512 VGPRs, two waves per workgroup, and refill LDS asynchronously (direct-to-LDS
-// loads into a second buffer while the current one is consumed).
-//
-// Every MFMA operand is one 16-byte LDS read: operands that reduce over head_dim come from
-// natural tiles; operands that reduce over rows come from TP tiles prepared in global memory
+// Every wave owns 32 rows (one 32x32 MFMA block); waves of a workgroup share K / V / Q / dO
+// tiles that direct-to-LDS loads stage through a ring of LDS buffers while earlier tiles are
+// consumed.  Every MFMA operand is one 16-byte LDS read: operands that reduce over head_dim come
+// from natural tiles; operands that reduce over rows come from TP tiles prepared in global memory
 // (see tiles64.h), so no transpose happens inside the hot loops.
 //
 //   k_pack_tp   kept rows of K / V / Q (head h) -> TP tiles [D][32] in a workspace
 //   k_fwd64     forward:   S^T = K Q^T, online softmax per query (lane-local), O^T += V^T P^T
 //   k_prep64    backward prologue per segment: D_i = dO_i.O_i, dOut -> bf16 natural + TP
-//   k_dkdv64    key-major:  S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q
+//   k_dkdv32    key-major:   S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q
 //   k_dq64      query-major: S^T = K Q^T, dP^T = V dO^T, dQ += dS K   (no atomics)
 #include "common.h"
 #include "kernels.h"
@@ -116,7 +111,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
   const int nsteps = qlast / 32 + 1;
   stage_kept(ktab, kept, qlast / p.block + 1);
   __syncthreads();
-  const KeptTab kt{ktab, kept, p.block};
+  const KeptTab kt{(const LDS_AS int*)ktab, kept, p.block};
 
   bf16x8 qf[NB][C::NS];
   int qpos[NB];
@@ -130,6 +125,10 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
       for (int s = 0; s < C::NS; ++s) qf[qb][s] = *(const bf16x8*)(qrow + (16 * s + 8 * hl) * 2);
     }
   }
+  // retire the register operand loads now: a load still pending when the staged loop starts
+  // would make the compiler wait for all vector memory, prefetched tiles included, at its first
+  // use in every iteration
+  wait_all_mem();
   f32x16 o[NB][C::NDB];
 #pragma unroll
   for (int qb = 0; qb < NB; ++qb)
@@ -153,9 +152,10 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
   ReadPlan<D> rp;
   rp.init();
 
+  const rsrc_t rk = make_rsrc(kbase), rv = make_rsrc(vtp);
   auto issue = [&](int step, char* buf) {
-    kplan.issue(buf, kbase + (int64_t)kt.pos(step * 32) * kstride);
-    vplan.issue(buf + OFF_V, vtp + (int64_t)step * C::TP32);
+    kplan.issue(buf, rk, (uint32_t)(kt.pos_u(step * 32) * kstride));
+    vplan.issue(buf + OFF_V, rv, (uint32_t)(step * C::TP32));
   };
 
   auto compute = [&](int step, const char* buf) {
@@ -220,14 +220,16 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
 
   // three-buffer ring: the tiles of step t+2 load while step t computes
   auto stage = [&](int t, const char* cur, char* nxt) {
-    if (!DC::EXACT || t + 1 >= nsteps) wait_all_mem();
+    // every step issues one tile (past the end, a reload of the last one that nobody reads), so
+    // exactly one tile's loads may still be in flight when tile t is needed
+    if (!DC::EXACT) wait_all_mem();
     else wait_vm<PER>();
-    __syncthreads();
-    if (t + 2 < nsteps) issue(t + 2, nxt);
+    stage_barrier();
+    issue(min(t + 2, nsteps - 1), nxt);
     compute(t, cur);
   };
   issue(0, sA);
-  if (nsteps > 1) issue(1, sB);
+  issue(min(1, nsteps - 1), sB);
   for (int t = 0; t < nsteps; t += 3) {
     stage(t, sA, sC);
     if (t + 1 >= nsteps) break;
@@ -235,6 +237,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
     if (t + 2 >= nsteps) break;
     stage(t + 2, sC, sB);
   }
+  wait_all_mem();                                        // drain the trailing reloads
 
   if (!active) return;
 #pragma unroll
@@ -368,17 +371,17 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
   const bool key_valid = kw0 < Nk;                               // Nk is a multiple of 64
   stage_kept(ktab, kept, (max(qe, min(k0 + KEYS, Nk)) - 1) / p.block + 1);
   __syncthreads();
-  const KeptTab kt{ktab, kept, p.block};
+  const KeptTab kt{(const LDS_AS int*)ktab, kept, p.block};
 
   const int64_t kstride = p.ks[1] * 2, qstride = p.qs[1] * 2;
   const int64_t dostride = (int64_t)p.Hq * D * 2;
   {
     NatPlan<D, NW> kp;
     kp.init(kstride);
-    const char* kbase = (const char*)((const bf16*)p.k + b * p.ks[0] + g * p.ks[2]);
+    const rsrc_t rkk = make_rsrc((const bf16*)p.k + b * p.ks[0] + g * p.ks[2]);
 #pragma unroll
     for (int t = 0; t < NW; ++t)
-      if (k0 + 32 * t < Nk) kp.issue(sK + t * C::NAT32, kbase + (int64_t)kt.pos(k0 + 32 * t) * kstride);
+      if (k0 + 32 * t < Nk) kp.issue(sK + t * C::NAT32, rkk, (uint32_t)(kt.pos_u(k0 + 32 * t) * kstride));
   }
   const char* Kw = sK + w * C::NAT32;                            // this wave's 32 key rows
   bf16x8 vf[C::NS];
@@ -388,6 +391,10 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) vf[s] = *(const bf16x8*)(vr + (16 * s + 8 * hl) * 2);
   }
+  // retire the register operand loads now: a load still pending when the staged loop starts
+  // would make the compiler wait for all vector memory, prefetched tiles included, at its first
+  // use in every iteration
+  wait_all_mem();
   f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) {
@@ -410,21 +417,27 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
   static_assert(16 % NW == 0, "lse/D chunks must split evenly over the waves");
   const int ld_chunk = LDC * w + l;
 
+  const rsrc_t rq = make_rsrc((const bf16*)p.q + b * p.qs[0]);
+  const rsrc_t rdo = make_rsrc((const char*)p.wsdO + (int64_t)b * p.seg_len * p.Hq * D * 2);
+  const rsrc_t rqt = make_rsrc((const char*)p.qtp + (int64_t)b * p.Hq * (p.seg_len / 32) * C::TP32);
+  const rsrc_t rdot = make_rsrc((const char*)p.dotp + (int64_t)b * p.Hq * (p.seg_len / 32) * C::TP32);
+  // lse2 and D rows of a step, one 16-byte chunk per lane l < LDC: lse2 chunks 0..7, D 8..15,
+  // both addressed from the D array of batch row b (the lse2 array follows it in the workspace)
+  const rsrc_t rld = make_rsrc(p.wsD + (int64_t)b * p.Hq * p.seg_len);
+  const uint32_t ld_voff = ld_chunk < 8 ? (uint32_t)((const char*)p.wsL2 - (const char*)p.wsD) + 16u * ld_chunk
+                                        : 16u * (ld_chunk - 8);
+
   auto issue = [&](int step, char* buf) {
     const int hh = step / nq;
     const int q0 = qstart + (step - hh * nq) * 32;
     const int h = g * G + hh;
-    qplan.issue(buf + OFF_Q, (const char*)((const bf16*)p.q + b * p.qs[0] + h * p.qs[2]) +
-                                 (int64_t)kt.pos(q0) * qstride);
-    dplan.issue(buf + OFF_DO, (const char*)p.wsdO + ((((int64_t)b * p.seg_len + (q0 - qs)) * p.Hq + h) * D) * 2);
-    const int64_t tile = ((int64_t)b * p.Hq + h) * (p.seg_len / 32) + (q0 - qs) / 32;
-    tplan.issue(buf + OFF_QT, (const char*)p.qtp + tile * C::TP32);
-    tplan.issue(buf + OFF_DOT, (const char*)p.dotp + tile * C::TP32);
-    if (l < LDC) {
-      const int64_t rowoff = ((int64_t)b * p.Hq + h) * p.seg_len + (q0 - qs);
-      const float* src = ld_chunk < 8 ? p.wsL2 + rowoff + 4 * ld_chunk : p.wsD + rowoff + 4 * (ld_chunk - 8);
-      dma16(src, buf + OFF_LD + 16 * LDC * w);
-    }
+    qplan.issue(buf + OFF_Q, rq, (uint32_t)((h * p.qs[2] + (int64_t)kt.pos_u(q0) * p.qs[1]) * 2));
+    dplan.issue(buf + OFF_DO, rdo, (uint32_t)(((int64_t)(q0 - qs) * p.Hq + h) * D * 2));
+    const uint32_t tile = (uint32_t)((h * (p.seg_len / 32) + (q0 - qs) / 32) * C::TP32);
+    tplan.issue(buf + OFF_QT, rqt, tile);
+    tplan.issue(buf + OFF_DOT, rdot, tile);
+    if (l < LDC)
+      dma16b(rld, ld_voff, (uint32_t)((h * p.seg_len + (q0 - qs)) * 4), buf + OFF_LD + 16 * LDC * w);
   };
 
   auto compute = [&](int step, const char* buf) {
@@ -484,12 +497,12 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
       if (step + 1 < nsteps) issue(step + 1, sB);
       compute(step, sA);
       wait_all_mem();
-      __syncthreads();
+      stage_barrier();
       if (step + 1 >= nsteps) break;
       if (step + 2 < nsteps) issue(step + 2, sA);
       compute(step + 1, sB);
       wait_all_mem();
-      __syncthreads();
+      stage_barrier();
     }
   }
 
@@ -555,7 +568,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
   const int nsteps = qlast / 32 + 1;
   stage_kept(ktab, kept, qlast / p.block + 1);
   __syncthreads();
-  const KeptTab kt{ktab, kept, p.block};
+  const KeptTab kt{(const LDS_AS int*)ktab, kept, p.block};
 
   bf16x8 qf[NB][C::NS], df[NB][C::NS];
   float lse2[NB], Dv[NB];
@@ -575,6 +588,10 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
       Dv[qb] = p.wsD[((int64_t)b * p.Hq + h) * p.seg_len + (qr - qs)];
     }
   }
+  // retire the register operand loads now: a load still pending when the staged loop starts
+  // would make the compiler wait for all vector memory, prefetched tiles included, at its first
+  // use in every iteration
+  wait_all_mem();
   f32x16 acc[NB][C::NDB];
 #pragma unroll
   for (int qb = 0; qb < NB; ++qb)
@@ -593,11 +610,12 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
   ReadPlan<D> rp;
   rp.init();
 
+  const rsrc_t rk = make_rsrc(kbase), rv = make_rsrc(vbase), rkt = make_rsrc(ktp);
   auto issue = [&](int step, char* buf) {
-    const int pos0 = kt.pos(step * 32);
-    kplan.issue(buf + OFF_K, kbase + (int64_t)pos0 * kstride);
-    vplan.issue(buf + OFF_V, vbase + (int64_t)pos0 * vstride);
-    tplan.issue(buf + OFF_KT, ktp + (int64_t)step * C::TP32);
+    const int pos0 = kt.pos_u(step * 32);
+    kplan.issue(buf + OFF_K, rk, (uint32_t)(pos0 * kstride));
+    vplan.issue(buf + OFF_V, rv, (uint32_t)(pos0 * vstride));
+    tplan.issue(buf + OFF_KT, rkt, (uint32_t)(step * C::TP32));
   };
 
   auto compute = [&](int step, const char* buf) {
@@ -650,14 +668,16 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
   };
 
   auto stage = [&](int t, const char* cur, char* nxt) {
-    if (!DC::EXACT || t + 1 >= nsteps) wait_all_mem();
+    // every step issues one tile (past the end, a reload of the last one that nobody reads), so
+    // exactly one tile's loads may still be in flight when tile t is needed
+    if (!DC::EXACT) wait_all_mem();
     else wait_vm<PER>();
-    __syncthreads();
-    if (t + 2 < nsteps) issue(t + 2, nxt);
+    stage_barrier();
+    issue(min(t + 2, nsteps - 1), nxt);
     compute(t, cur);
   };
   issue(0, sA);
-  if (nsteps > 1) issue(1, sB);
+  issue(min(1, nsteps - 1), sB);
   for (int t = 0; t < nsteps; t += 3) {
     stage(t, sA, sC);
     if (t + 1 >= nsteps) break;
@@ -665,6 +685,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
     if (t + 2 >= nsteps) break;
     stage(t + 2, sC, sB);
   }
+  wait_all_mem();                                        // drain the trailing reloads
 
   if (!active) return;
   // dQ accumulator: lane holds head_dim column db*32 + lc of queries 8(r/4)+4hl+r%4

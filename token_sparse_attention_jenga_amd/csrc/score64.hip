@@ -45,6 +45,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) qf[s] = *(const bf16x8*)(qrow + (16 * s + 8 * hl) * 2);
   }
+  // retire the register operand loads now: a load still pending when the staged loop starts
+  // would make the compiler wait for all vector memory, prefetched tiles included, at its first
+  // use in every iteration
+  wait_all_mem();
   const char* kbase = (const char*)((const bf16*)p.k + b * p.ks[0] + g * p.ks[2]);
   const int64_t kstride = p.ks[1] * 2;
   NatPlan<D, NW> kplan;
@@ -55,7 +59,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
   float m_run = -INFINITY;
   double l_run = 0.0;
 
-  auto issue = [&](int t, char* buf) { kplan.issue(buf, kbase + (int64_t)(32 * t) * kstride); };
+  const rsrc_t rk = make_rsrc(kbase);
+  auto issue = [&](int t, char* buf) { kplan.issue(buf, rk, (uint32_t)(32 * t * kstride)); };
   auto compute = [&](int t, const char* Kl) {
     const int kr0 = 32 * t;
     if (!active || kr0 > qw0 + 31) return;
@@ -82,14 +87,16 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
     l_run += (double)rs;
   };
   auto stage = [&](int t, const char* cur, char* nxt) {
-    if (!DC::EXACT || t + 1 >= nsteps) wait_all_mem();
+    // every step issues one tile (past the end, a reload of the last one that nobody reads), so
+    // exactly one tile's loads may still be in flight when tile t is needed
+    if (!DC::EXACT) wait_all_mem();
     else wait_vm<PER>();
-    __syncthreads();
-    if (t + 2 < nsteps) issue(t + 2, nxt);
+    stage_barrier();
+    issue(min(t + 2, nsteps - 1), nxt);
     compute(t, cur);
   };
   issue(0, sA);
-  if (nsteps > 1) issue(1, sB);
+  issue(min(1, nsteps - 1), sB);
   for (int t = 0; t < nsteps; t += 3) {
     stage(t, sA, sC);
     if (t + 1 >= nsteps) break;
@@ -97,6 +104,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
     if (t + 2 >= nsteps) break;
     stage(t + 2, sC, sB);
   }
+  wait_all_mem();                                        // drain the trailing reloads
   if (!active) return;
   const double lsum = l_run + __shfl_xor(l_run, 32, 64);
   if (hl == 0) p.lse2[((int64_t)b * p.Hq + h) * p.S + qi] = (float)((double)m_run + log2(lsum));
@@ -131,6 +139,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_smass64(ScoreParams p) {
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) kf[s] = *(const bf16x8*)(krow + (16 * s + 8 * hl) * 2);
   }
+  // retire the register operand loads now: a load still pending when the staged loop starts
+  // would make the compiler wait for all vector memory, prefetched tiles included, at its first
+  // use in every iteration
+  wait_all_mem();
   const char* qbase = (const char*)((const bf16*)p.q + b * p.qs[0] + h * p.qs[2]);
   const int64_t qstride = p.qs[1] * 2;
   const float* lrow = p.lse2 + ((int64_t)b * p.Hq + h) * p.S;
@@ -141,10 +153,12 @@ __global__ __launch_bounds__(64 * NW, 2) void k_smass64(ScoreParams p) {
   const float c2 = p.scale_log2;
   double acc = 0.0;
 
+  const rsrc_t rq = make_rsrc(qbase), rl = make_rsrc(lrow);
+  const uint32_t lvoff = 16u * (LDC * w + l);
   auto issue = [&](int t, char* buf) {
     const int q0 = k0 + 32 * t;
-    qplan.issue(buf, qbase + (int64_t)q0 * qstride);
-    if (l < LDC) dma16(lrow + q0 + 4 * (LDC * w + l), buf + C::NAT32 + 16 * LDC * w);
+    qplan.issue(buf, rq, (uint32_t)(q0 * qstride));
+    if (l < LDC) dma16b(rl, lvoff, (uint32_t)q0 * 4u, buf + C::NAT32 + 16 * LDC * w);
   };
   auto compute = [&](int t, const char* buf) {
     const int q0 = k0 + 32 * t;
@@ -175,15 +189,17 @@ __global__ __launch_bounds__(64 * NW, 2) void k_smass64(ScoreParams p) {
     acc += (double)colsum;
   };
   auto stage = [&](int t, const char* cur, char* nxt) {
-    if (!DC::EXACT || t + 1 >= nsteps) wait_all_mem();
+    // every step issues one tile (past the end, a reload of the last one that nobody reads), so
+    // exactly one tile's loads may still be in flight when tile t is needed
+    if (!DC::EXACT) wait_all_mem();
     else wait_vm<PER>();
-    __syncthreads();
-    if (t + 2 < nsteps) issue(t + 2, nxt);
+    stage_barrier();
+    issue(min(t + 2, nsteps - 1), nxt);
     compute(t, cur);
   };
   if (nsteps > 0) {
     issue(0, sA);
-    if (nsteps > 1) issue(1, sB);
+    issue(min(1, nsteps - 1), sB);
     for (int t = 0; t < nsteps; t += 3) {
       stage(t, sA, sC);
       if (t + 1 >= nsteps) break;
@@ -192,6 +208,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_smass64(ScoreParams p) {
       stage(t + 2, sC, sB);
     }
   }
+  wait_all_mem();                                        // drain the trailing reloads
   // lanes l and l^32 hold the same key; then a fixed butterfly over the wave's 32 keys
   acc += __shfl_xor(acc, 32, 64);
 #pragma unroll

@@ -36,6 +36,23 @@ __device__ inline void dma16(const void* g, char* lds) {
   __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)lds, 16, 0, 0);
 }
 
+// Direct-to-LDS copies through raw buffer loads.  The resource holds a wave-uniform base (kept in
+// SGPRs); a copy adds a per-lane offset (voff, a register computed once per kernel) and a
+// wave-uniform one (soff, per step).  Keeping the per-lane part in a long-lived register matters:
+// when a 64-bit address register of an outstanding direct-to-LDS load is reused, the compiler
+// first waits for all outstanding vector-memory work, prefetched tiles included.  Every caller
+// keeps voff + soff inside the tensor the base points into (below 4 GiB); the range field is
+// not relied on.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ inline rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+
+__device__ inline void dma16b(rsrc_t r, uint32_t voff, uint32_t soff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, voff, soff, 0, 0);
+}
+
 // Wait for every outstanding memory operation of this wave (direct-to-LDS loads included).
 __device__ inline void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -45,6 +62,19 @@ template <int N>
 __device__ inline void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the staged loops.  __syncthreads() also fences memory, which makes
+// the compiler wait for every outstanding vector-memory operation -- including the
+// direct-to-LDS loads of tiles still being prefetched.  Here each wave first waits for its own
+// loads of the tile about to be read (the caller's wait_vm / wait_all_mem) and for its LDS
+// reads of the tile about to be overwritten; the asm memory clobbers keep the compiler from
+// moving LDS accesses across the barrier.
+__device__ inline void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0) only
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Direct-to-LDS instructions one wave issues for a tile (uniform across waves iff exact).
@@ -88,12 +118,15 @@ __device__ inline void dma_tp32(char* lds_tile, const char* g_tile) {
 }
 
 // Per-lane address offsets of one wave's direct-to-LDS instructions, computed once per kernel
-// so that a step only adds its (wave-uniform) base address.
+// so that a step only adds its (wave-uniform) base address.  The offsets are unsigned 32-bit so
+// that the loads take the scalar-base form (uniform base in SGPRs + per-lane offset register):
+// with a fresh 64-bit address register per load, the compiler waits for every outstanding
+// vector-memory operation before it may reuse that register.
 template <int D, int NW>
 struct NatPlan {
   static constexpr int NI = DmaCount<D, NW>::NAT;
   static constexpr int MAXW = (NI + NW - 1) / NW;
-  int off[MAXW];
+  uint32_t off[MAXW];
   __device__ void init(int64_t row_stride) {
     constexpr int CPR = T64<D>::CPR;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -101,14 +134,15 @@ struct NatPlan {
     for (int i = 0; i < MAXW; ++i) {
       const int idx = (w + i * NW) * 64 + l;
       const int row = idx / CPR, phys = idx % CPR;
-      off[i] = (int)(row * row_stride) + ((phys ^ (row & (CPR - 1))) << 4);
+      off[i] = (uint32_t)(row * row_stride) + ((phys ^ (row & (CPR - 1))) << 4);
     }
   }
-  __device__ void issue(char* lds_tile, const char* g_row0) const {
+  // rows at byte offset soff (row 0) from the resource's base
+  __device__ void issue(char* lds_tile, rsrc_t r, uint32_t soff) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < MAXW; ++i)
-      if (w + i * NW < NI) dma16(g_row0 + off[i], lds_tile + (w + i * NW) * 1024);
+      if (w + i * NW < NI) dma16b(r, off[i], soff, lds_tile + (w + i * NW) * 1024);
   }
 };
 
@@ -116,21 +150,22 @@ template <int D, int NW>
 struct TpPlan {
   static constexpr int NI = DmaCount<D, NW>::TP;
   static constexpr int MAXW = (NI + NW - 1) / NW;
-  int off[MAXW];
+  uint32_t off[MAXW];
   __device__ void init() {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < MAXW; ++i) {
       const int idx = (w + i * NW) * 64 + l;
       const int d = idx >> 2, phys = idx & 3;
-      off[i] = d * 64 + ((phys ^ tpswz(d)) << 4);
+      off[i] = (uint32_t)(d * 64 + ((phys ^ tpswz(d)) << 4));
     }
   }
-  __device__ void issue(char* lds_tile, const char* g_tile) const {
+  // the TP tile at byte offset soff from the resource's base
+  __device__ void issue(char* lds_tile, rsrc_t r, uint32_t soff) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < MAXW; ++i)
-      if (w + i * NW < NI) dma16(g_tile + off[i], lds_tile + (w + i * NW) * 1024);
+      if (w + i * NW < NI) dma16b(r, off[i], soff, lds_tile + (w + i * NW) * 1024);
   }
 };
 
@@ -168,12 +203,31 @@ __device__ inline bf16x8 ld_tp(const char* tile, int d, int c) {
 constexpr int kKeptTab = 1024;
 
 struct KeptTab {
-  const int* s;            // LDS copy of kept[0 .. min(n, kKeptTab))
+  const LDS_AS int* s;     // LDS copy of kept[0 .. min(n, kKeptTab))
   const int32_t* g;        // the global list
   int block;
+  // The table is typed as LDS so that the two reads stay an LDS read and a global read: merged
+  // into one flat load, every lookup would also wait for all outstanding vector-memory work,
+  // including tiles still being prefetched.
   __device__ int pos(int r) const {
     const int kb = r / block;
-    return (kb < kKeptTab ? s[kb] : g[kb]) * block + (r - kb * block);
+    const int v = kb < kKeptTab ? s[kb] : g[kb];
+    return v * block + (r - kb * block);
+  }
+  // The same for a wave-uniform rank, as used by the staged loops.  Each branch ends in a scalar
+  // register, and the global branch waits for its own load: were the two joined in one vector
+  // register, the common path would wait for every outstanding vector-memory operation.
+  __device__ int pos_u(int r) const {
+    const int kb = r / block;
+    int v;
+    if (kb < kKeptTab) {
+      v = __builtin_amdgcn_readfirstlane(s[kb]);
+    } else {
+      const int x = g[kb];
+      __builtin_amdgcn_s_waitcnt(0);
+      v = __builtin_amdgcn_readfirstlane(x);
+    }
+    return v * block + (r - kb * block);
   }
 };
 
