@@ -120,6 +120,50 @@ def block_scores(q, k, block: int, scale: float = None) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------
+# Eq. 2 literal scoring ([summary] 4.2.2 Eq. 2, 4.2.3): informativeness of a score block is the
+# maximum, over its elements, of the head-averaged *positive* attention scores; a key block's
+# score sums its score blocks over the query blocks.
+# ----------------------------------------------------------------------------------------
+
+def eq2_tile_max(q, k, block: int, b: int, m: int, n: int, scale: float = None) -> float:
+    """I(B^S) of the score block with query block m and key block n (m >= n) of batch row b.
+
+    Per element (i, j): e_ij = (1/Hq) * sum over heads of max(scale * q_i . k_j, 0) -- only
+    positive scores enter the head aggregation -- then the maximum over the block's elements
+    with j <= i (causal; on the diagonal block the masked upper triangle does not take part).
+    """
+    q, k = _f64(q), _f64(k)
+    _, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = default_scale(D)
+    qi = np.arange(m * block, (m + 1) * block)
+    kj = np.arange(n * block, (n + 1) * block)
+    e = np.zeros((block, block))
+    for h in range(Hq):
+        g = kv_head_of(h, Hq, Hkv)
+        sc = scale * (q[b, qi, h, :] @ k[b, kj, g, :].T)
+        e += np.maximum(sc, 0.0)
+    e /= Hq
+    allowed = kj[None, :] <= qi[:, None]
+    return float(e[allowed].max())
+
+
+def block_scores_eq2(q, k, block: int, scale: float = None, key_blocks=None) -> np.ndarray:
+    """s[b, n] = sum over query blocks m >= n of eq2_tile_max(m, n)  ([summary] 4.2.3: the
+    token-block score aggregates its score blocks; the causal mask leaves only m >= n).
+    key_blocks restricts the computation to those n (other entries are NaN)."""
+    B, S = q.shape[0], q.shape[1]
+    nkb = S // block
+    ns = range(nkb) if key_blocks is None else key_blocks
+    out = np.full((B, nkb), np.nan)
+    for b in range(B):
+        for n in ns:
+            out[b, n] = sum(eq2_tile_max(q, k, block, b, m, n, scale) for m in range(n, nkb))
+    return out
+
+
+# ----------------------------------------------------------------------------------------
 # Selection ([notes] 4.2 layer-specific threshold, Algorithm 1 step 1; top-k by keep ratio)
 # ----------------------------------------------------------------------------------------
 
