@@ -28,8 +28,8 @@ if ROOT not in sys.path:
 
 BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 bf16 flop/clk/CU x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
-KERNELS = ("k_slse64", "k_smass64", "k_select", "k_pack_tp", "k_fwd64", "k_prep64", "k_dkdv32",
-           "k_dq64")
+KERNELS = ("k_slse64", "k_smass64", "k_eq2_tiles", "k_eq2_reduce", "k_select", "k_pack_tp",
+           "k_fwd64", "k_prep64", "k_dkdv32", "k_dq64")
 METRIC = "fwd+bwd token-sparse attn TFLOP/s (kept FLOPs) & tokens/s at S=32K; % MFMA peak"
 
 
@@ -308,6 +308,34 @@ def main():
                     "avg_launch_us": round(avg_ms * 1e3, 2)}
     kernel_avg_us = {kk: {"launches": n, "avg_us": round(1e3 * t / n, 2)} for kk, (n, t) in kern_ms.items()}
 
+    # Eq. 2 literal scoring (the NEXT-row scoring mode), timed on its own after the steps: one
+    # call per layer, MFMA work 2*D*Hq per element of every causal score block
+    eq2 = None
+    if cfg.dtype == "bf16" and blk in (64, 128):
+        p0 = layers[0]["p"]
+        ws_e = J.alloc_workspace(J.workspace_bytes(p0, J.JENGA_OP_SCORE_EQ2), dev)
+        sc_e = torch.empty((B, nkb), dtype=torch.float32, device=dev)
+        for st in layers:                                              # warm-up
+            J.jenga_score_blocks_eq2(st["p"], st["q"], st["k"], sc_e, ws_e)
+        torch.cuda.synchronize()
+        J.timing_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            for st in layers:
+                J.jenga_score_blocks_eq2(st["p"], st["q"], st["k"], sc_e, ws_e)
+        e1.record(stream)
+        J.timing_enable(False)
+        torch.cuda.synchronize()
+        eq2_ms = e0.elapsed_time(e1) / (K * L)
+        eq2_flop = 2.0 * D * Hq * B * blk * blk * nkb * (nkb + 1) / 2
+        n_t, t_t = J.timing_query("k_eq2_tiles")
+        eq2 = {"ms_per_layer": round(eq2_ms, 4), "tflops": round(eq2_flop / (eq2_ms * 1e-3) / 1e12, 2),
+               "pct_bf16_mfma_peak": round(100 * eq2_flop / (eq2_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
+               "k_eq2_tiles_avg_us": round(1e3 * t_t / max(n_t, 1), 2),
+               "work": "2*D*Hq flop per element of every causal b x b score block"}
+        del ws_e, sc_e
+
     copy_ms = None
     if args.copy_calibration:
         # plain elementwise copy (16-byte vector loads/stores), 1 GiB read + 1 GiB written
@@ -359,6 +387,7 @@ def main():
         "bwd_tflops": round(bwd_flop / (phase["bwd"] * 1e-3) / 1e12, 2),
         "score_tflops_algorithmic": round(score_flop / (phase["score"] * 1e-3) / 1e12, 2),
         "kept_tokens_per_layer": nks,
+        "eq2_scoring": eq2,
         "roofline": roofline,
         "kernel_avg_us": kernel_avg_us,
         "cpu_baseline": cpu,

@@ -51,7 +51,7 @@ typedef enum {
 
 #define JENGA_FORCE_FIRST_BLOCK 1u  /* flag: block 0 is always kept */
 
-typedef enum { JENGA_OP_SCORE = 0, JENGA_OP_FWD = 1, JENGA_OP_BWD = 2 } jenga_op;
+typedef enum { JENGA_OP_SCORE = 0, JENGA_OP_FWD = 1, JENGA_OP_BWD = 2, JENGA_OP_SCORE_EQ2 = 3 } jenga_op;
 
 /* Problem shape, shared by every call of one layer. */
 typedef struct jenga_problem {
@@ -98,6 +98,28 @@ size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks
  */
 int jenga_score_blocks(const jenga_problem* p, const void* q, const void* k, float* block_scores,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * jenga_score_blocks_eq2 — the literal form of [summary] 4.2.2 Eq. 2 and 4.2.3: a score block's
+ * informativeness is the maximum over its elements of the head-averaged positive attention
+ * scores, and a key block's score sums its score blocks over the query blocks.
+ *
+ * For every batch row and key block n, with query block m >= n (causal):
+ *   e_ij = (1/Hq) sum_h max(scale * q_i^h . k_j^(h/(Hq/Hkv)), 0)
+ *   B(m, n) = max over i in block m, j in block n, j <= i of e_ij
+ *   block_scores[b][n] = sum_{m >= n} B(m, n)
+ * One pass over the causal score blocks without exponentials; deterministic (the sum over m
+ * is fp64 in ascending m).  bf16 only, block 64 or 128, head_dim 64 or 128.
+ *
+ *   q, k         as for jenga_score_blocks
+ *   block_scores [B][S/block] fp32, dense, written
+ *   workspace    >= jenga_workspace_bytes(p, JENGA_OP_SCORE_EQ2, 0, 1) = B * nKB^2 * 4 bytes
+ *                (rounded up), 256-byte aligned
+ * Errors: UNSUPPORTED for fp32 or another block size; otherwise as jenga_score_blocks.
+ */
+int jenga_score_blocks_eq2(const jenga_problem* p, const void* q, const void* k,
+                           float* block_scores, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * jenga_select_blocks — token-block elimination against a per-layer threshold or a keep
@@ -187,7 +209,7 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
  * jenga_timing_enable(1) discards earlier records and, from then on, brackets every kernel
  * launched by the entry points above with two HIP events recorded on that call's stream;
  * jenga_timing_enable(0) stops recording (the records stay readable).  Kernel names:
- * k_slse64, k_smass64 (bf16 scoring), k_select, k_pack_tp, k_fwd64, k_prep64, k_dkdv32,
+ * k_slse64, k_smass64 (bf16 scoring), k_eq2_tiles, k_eq2_reduce (Eq. 2 scoring), k_select, k_pack_tp, k_fwd64, k_prep64, k_dkdv32,
  * k_dq64 (bf16 attention).  The fp32 kernels are not bracketed.
  *
  * jenga_timing_query(kernel, launches, total_ms) waits for the recorded events of that name

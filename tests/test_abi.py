@@ -143,3 +143,15 @@ def test_timing_calls_without_gpu_work(J):
     J.timing_enable(False)
     n = ctypes.c_int32(0)
     assert J.lib.jenga_timing_query(None, ctypes.byref(n), None) == J.JENGA_ERR_INVALID_ARG
+
+
+def test_score_eq2_validation(J):
+    p = _problem(J, D=128, dtype=1, block=64)
+    need = J.workspace_bytes(p, J.JENGA_OP_SCORE_EQ2)
+    assert need == 1 * 16 * 16 * 4 or need == 256        # B * nKB^2 fp32, 256-byte rounded
+    f = lambda pp=p, ws=FAKE, wsb=need: J.lib.jenga_score_blocks_eq2(ctypes.byref(pp), FAKE, FAKE, FAKE,
+                                                                    ws, wsb, None)
+    assert f(pp=_problem(J, D=64, dtype=0)) == J.JENGA_ERR_UNSUPPORTED          # fp32
+    assert f(pp=_problem(J, D=128, dtype=1, block=256)) == J.JENGA_ERR_UNSUPPORTED
+    assert f(wsb=need - 1) == J.JENGA_ERR_WORKSPACE
+    assert f(ws=0) == J.JENGA_ERR_WORKSPACE

@@ -27,10 +27,12 @@ JENGA_FORCE_FIRST_BLOCK = 1
 JENGA_OP_SCORE = 0
 JENGA_OP_FWD = 1
 JENGA_OP_BWD = 2
+JENGA_OP_SCORE_EQ2 = 3
 
 EXPORTED = ["jenga_status_string", "jenga_topk_count", "jenga_workspace_bytes",
-            "jenga_score_blocks", "jenga_select_blocks", "jenga_sparse_attn_fwd",
-            "jenga_sparse_attn_bwd_segmented", "jenga_timing_enable", "jenga_timing_query"]
+            "jenga_score_blocks", "jenga_score_blocks_eq2", "jenga_select_blocks",
+            "jenga_sparse_attn_fwd", "jenga_sparse_attn_bwd_segmented", "jenga_timing_enable",
+            "jenga_timing_query"]
 
 
 class JengaProblem(ctypes.Structure):
@@ -63,6 +65,8 @@ def _load() -> ctypes.CDLL:
     lib.jenga_workspace_bytes.restype = sz
     lib.jenga_score_blocks.argtypes = [P, vp, vp, vp, vp, sz, vp]
     lib.jenga_score_blocks.restype = i32
+    lib.jenga_score_blocks_eq2.argtypes = [P, vp, vp, vp, vp, sz, vp]
+    lib.jenga_score_blocks_eq2.restype = i32
     lib.jenga_select_blocks.argtypes = [P, vp, i32, ctypes.c_float, ctypes.c_uint, vp, vp, vp]
     lib.jenga_select_blocks.restype = i32
     lib.jenga_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
@@ -165,6 +169,13 @@ def jenga_score_blocks(p: JengaProblem, q, k, block_scores, workspace, stream=No
     _check("jenga_score_blocks", st)
 
 
+def jenga_score_blocks_eq2(p: JengaProblem, q, k, block_scores, workspace, stream=None) -> None:
+    st = lib.jenga_score_blocks_eq2(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(block_scores),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream))
+    _check("jenga_score_blocks_eq2", st)
+
+
 def jenga_select_blocks(p: JengaProblem, block_scores, mode: int, param: float, flags: int,
                         kept_idx, n_kept, stream=None) -> None:
     st = lib.jenga_select_blocks(ctypes.byref(p), _ptr(block_scores), int(mode),
@@ -203,6 +214,16 @@ def score_blocks(q, k, block: int, scale: float = 0.0):
     out = torch.empty((q.shape[0], q.shape[1] // block), dtype=torch.float32, device=q.device)
     ws = alloc_workspace(workspace_bytes(p, JENGA_OP_SCORE), q.device)
     jenga_score_blocks(p, q, k, out, ws)
+    return out
+
+
+def score_blocks_eq2(q, k, block: int, scale: float = 0.0):
+    """Eq. 2 literal block scores (positive head-mean, score-block maximum, sum over m >= n)."""
+    import torch
+    p = make_problem(q, k, None, block, scale)
+    out = torch.empty((q.shape[0], q.shape[1] // block), dtype=torch.float32, device=q.device)
+    ws = alloc_workspace(workspace_bytes(p, JENGA_OP_SCORE_EQ2), q.device)
+    jenga_score_blocks_eq2(p, q, k, out, ws)
     return out
 
 

@@ -89,6 +89,11 @@ size_t fwd_ws_bytes(const jenga_problem* p, int max_kept_blocks) {
   return align_up((size_t)p->batch * p->n_heads_kv * max_kept_blocks * p->block * p->head_dim * 2);
 }
 
+size_t score_eq2_ws_bytes(const jenga_problem* p) {
+  const size_t nkb = p->seq_len / p->block;
+  return align_up((size_t)p->batch * nkb * nkb * sizeof(float));
+}
+
 size_t score_ws_bytes(const jenga_problem* p) {
   const size_t lse = (size_t)p->batch * p->n_heads_q * p->seq_len * sizeof(float);
   const size_t mass = (size_t)p->batch * p->n_heads_q * (p->seq_len / 32) * sizeof(double);
@@ -123,6 +128,7 @@ int jenga_topk_count(float keep_ratio, int n_blocks) {
 size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks, int n_segments) {
   if (check_problem(p, false) != JENGA_OK) return 0;
   if (op == JENGA_OP_SCORE) return score_ws_bytes(p);
+  if (op == JENGA_OP_SCORE_EQ2) return score_eq2_ws_bytes(p);
   if (op == JENGA_OP_FWD) {
     const int nkb = p->seq_len / p->block;
     if (max_kept_blocks < 1 || max_kept_blocks > nkb) return 0;
@@ -162,6 +168,37 @@ int jenga_score_blocks(const jenga_problem* p, const void* q, const void* k, flo
                         align_up((size_t)p->batch * p->n_heads_q * p->seq_len * sizeof(float)));
   sp.scores = block_scores;
   if (jenga::launch_score(sp, p->dtype, p->head_dim, (hipStream_t)stream) != hipSuccess)
+    return JENGA_ERR_LAUNCH;
+  return JENGA_OK;
+}
+
+int jenga_score_blocks_eq2(const jenga_problem* p, const void* q, const void* k,
+                           float* block_scores, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  int st = check_problem(p, true);
+  if (st != JENGA_OK) return st;
+  if (p->dtype != JENGA_DTYPE_BF16) return JENGA_ERR_UNSUPPORTED;
+  if (p->block != 64 && p->block != 128) return JENGA_ERR_UNSUPPORTED;
+  if (!q || !k || !block_scores) return JENGA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k)) return JENGA_ERR_INVALID_ARG;
+  const size_t need = score_eq2_ws_bytes(p);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+    return JENGA_ERR_WORKSPACE;
+  jenga::Eq2Params ep;
+  ep.q = q;
+  ep.k = k;
+  copy_strides(ep.qs, p->q_stride);
+  copy_strides(ep.ks, p->k_stride);
+  ep.B = p->batch;
+  ep.S = p->seq_len;
+  ep.Hq = p->n_heads_q;
+  ep.Hkv = p->n_heads_kv;
+  ep.block = p->block;
+  ep.nkb = p->seq_len / p->block;
+  ep.scale = scale_of(p);
+  ep.tilemax = (float*)workspace;
+  ep.scores = block_scores;
+  if (jenga::launch_score_eq2(ep, p->head_dim, p->block, (hipStream_t)stream) != hipSuccess)
     return JENGA_ERR_LAUNCH;
   return JENGA_OK;
 }

@@ -1,0 +1,154 @@
+// Eq. 2 literal block scoring for gfx950 (bf16).
+//
+// Jenga (aipaper summary, §4.2.2 Eq. 2): the informativeness of a score block is the maximum,
+// over its elements, of the attention scores aggregated across heads, where only positive
+// scores enter the aggregation and the sum is divided by the number of heads; §4.2.3: a token
+// block's score sums its score blocks.  Here score block (m, n) pairs query block m with key
+// block n (m >= n, causal):
+//   e_ij = (1/Hq) sum_h max(c q_i^h . k_j^g(h), 0),  B(m,n) = max_{i in m, j in n, j <= i} e_ij,
+//   s_n  = sum_{m >= n} B(m,n).
+//
+//   k_eq2_tiles   one workgroup per causal score block: loops over the query heads, S^h = Q K^T
+//                 per 32x32 sub-tile with MFMA, acc += max(S^h, 0); then the causal mask on the
+//                 diagonal block and the block maximum, times c / Hq (c > 0 factors out of the
+//                 positive part and the maximum).  Q and K tiles of the next head load into a
+//                 second LDS buffer while the current head is processed.
+//   k_eq2_reduce  s_n = sum over m >= n in a fixed order (fp64), rounded once to fp32.
+#include "common.h"
+#include "kernels.h"
+#include "tiles64.h"
+
+namespace jenga {
+
+// Causal score block (m, n), m >= n, of linear index t in m-major order: t = m(m+1)/2 + n.
+__device__ inline void pair_of(int t, int& m, int& n) {
+  int mm = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+  while ((mm + 1) * (mm + 2) / 2 <= t) ++mm;
+  while (mm * (mm + 1) / 2 > t) --mm;
+  m = mm;
+  n = t - mm * (mm + 1) / 2;
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(256, 1) void k_eq2_tiles(Eq2Params p) {
+  using C = T64<D>;
+  constexpr int NW = 4;
+  constexpr int SB = BLK / 32;                            // 32-row sub-blocks per block
+  constexpr int SPW = SB * SB / NW;                       // sub-tiles per wave
+  static_assert(SPW >= 1 && SB * SB == SPW * NW, "block must be 64 or 128");
+  constexpr int STAGE = 2 * SB * C::NAT32;                // Q tiles then K tiles of one head
+  __shared__ __attribute__((aligned(1024))) char sA[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sB[STAGE];
+  __shared__ float wmax[NW];
+
+  const Tile3 tl = xcd_tile();
+  const int b = tl.y;
+  int m, n;
+  pair_of(tl.x, m, n);
+  const int G = p.Hq / p.Hkv;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
+
+  const int64_t qstride = p.qs[1] * 2, kstride = p.ks[1] * 2;
+  NatPlan<D, NW> qplan, kplan;
+  qplan.init(qstride);
+  kplan.init(kstride);
+  ReadPlan<D> rp;
+  rp.init();
+  const rsrc_t rq = make_rsrc((const bf16*)p.q + b * p.qs[0]);
+  const rsrc_t rk = make_rsrc((const bf16*)p.k + b * p.ks[0]);
+  auto issue = [&](int h, char* buf) {
+    const int g = h / G;
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      qplan.issue(buf + sb * C::NAT32, rq, (uint32_t)((h * p.qs[2] + (int64_t)(m * BLK + 32 * sb) * p.qs[1]) * 2));
+      kplan.issue(buf + (SB + sb) * C::NAT32, rk, (uint32_t)((g * p.ks[2] + (int64_t)(n * BLK + 32 * sb) * p.ks[1]) * 2));
+    }
+  };
+
+  f32x16 acc[SPW];
+#pragma unroll
+  for (int t = 0; t < SPW; ++t) acc[t] = zero16();
+  // sub-tile t of this wave: query sub-block qsb(t), key sub-block ksb(t)
+  auto qsb = [&](int t) { return (w * SPW + t) / SB; };
+  auto ksb = [&](int t) { return (w * SPW + t) % SB; };
+
+  auto compute = [&](const char* buf) {
+#pragma unroll
+    for (int t = 0; t < SPW; ++t) {
+      const char* Qt = buf + qsb(t) * C::NAT32;
+      const char* Kt = buf + (SB + ksb(t)) * C::NAT32;
+      f32x16 st = zero16();
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) st = Mfma<bf16>::mma(ldo(Qt, rp.nat[s]), ldo(Kt, rp.nat[s]), st);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] += fmaxf(st[r], 0.f);
+    }
+  };
+
+  issue(0, sA);
+  wait_all_mem();
+  __syncthreads();
+  for (int h = 0; h < p.Hq; h += 2) {
+    if (h + 1 < p.Hq) issue(h + 1, sB);
+    compute(sA);
+    wait_all_mem();
+    stage_barrier();
+    if (h + 1 >= p.Hq) break;
+    if (h + 2 < p.Hq) issue(h + 2, sA);
+    compute(sB);
+    wait_all_mem();
+    stage_barrier();
+  }
+
+  // lane = key n*BLK + 32 ksb + lc; register r = query m*BLK + 32 qsb + 8(r/4) + 4hl + r%4.
+  // Every e >= 0, so a masked element set to 0 cannot raise the maximum.
+  float mx = 0.f;
+#pragma unroll
+  for (int t = 0; t < SPW; ++t) {
+    const int qrow0 = 32 * qsb(t) + 4 * hl, kcol = 32 * ksb(t) + lc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool masked = m == n && kcol > qrow0 + 8 * (r >> 2) + (r & 3);
+      mx = fmaxf(mx, masked ? 0.f : acc[t][r]);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (l == 0) wmax[w] = mx;
+  __syncthreads();
+  if (tid == 0) {
+    float v = wmax[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) v = fmaxf(v, wmax[i]);
+    p.tilemax[((int64_t)b * p.nkb + m) * p.nkb + n] = v * p.scale / (float)p.Hq;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_eq2_reduce(Eq2Params p) {
+  const int b = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= p.nkb) return;
+  double s = 0.0;
+  for (int m = n; m < p.nkb; ++m) s += (double)p.tilemax[((int64_t)b * p.nkb + m) * p.nkb + n];
+  p.scores[(int64_t)b * p.nkb + n] = (float)s;
+}
+
+template <int D, int BLK>
+static hipError_t launch_eq2_t(const Eq2Params& p, hipStream_t st) {
+  const int pairs = p.nkb * (p.nkb + 1) / 2;
+  {
+    TimedLaunch tl("k_eq2_tiles", st);
+    k_eq2_tiles<D, BLK><<<dim3(pairs, p.B), 256, 0, st>>>(p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  TimedLaunch tl("k_eq2_reduce", st);
+  k_eq2_reduce<<<dim3((p.nkb + 255) / 256, p.B), 256, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_eq2(const Eq2Params& p, int D, int block, hipStream_t st) {
+  if (D == 64) return block == 64 ? launch_eq2_t<64, 64>(p, st) : launch_eq2_t<64, 128>(p, st);
+  return block == 64 ? launch_eq2_t<128, 64>(p, st) : launch_eq2_t<128, 128>(p, st);
+}
+
+}  // namespace jenga

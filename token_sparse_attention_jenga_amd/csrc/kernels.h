@@ -17,6 +17,16 @@ struct ScoreParams {
   float* scores;      // [B][S/block]
 };
 
+struct Eq2Params {
+  const void* q;
+  const void* k;
+  int64_t qs[3], ks[3];
+  int B, S, Hq, Hkv, block, nkb;
+  float scale;        // softmax scale
+  float* tilemax;     // workspace [B][nkb][nkb]: score-block maxima (query block, key block)
+  float* scores;      // [B][nkb]
+};
+
 struct SelectParams {
   const float* scores;
   int B, nkb, mode, kcount;
@@ -72,6 +82,9 @@ hipError_t launch_bwd_segment(const BwdParams& p, int dtype, int D, hipStream_t 
 
 // bf16 scoring with async LDS staging (score64.hip)
 hipError_t launch_score64(const ScoreParams& p, int D, hipStream_t st);
+
+// bf16 Eq. 2 literal scoring (eq2.hip): block 64 or 128
+hipError_t launch_score_eq2(const Eq2Params& p, int D, int block, hipStream_t st);
 
 // Per-kernel event timing (timing.cpp).  A TimedLaunch placed around a launch records a start
 // event on construction and a stop event on destruction when timing is enabled.
