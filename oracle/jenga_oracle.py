@@ -164,6 +164,43 @@ def block_scores_eq2(q, k, block: int, scale: float = None, key_blocks=None) -> 
 
 
 # ----------------------------------------------------------------------------------------
+# Permutation-free token movement around the projections ([notes] 4.4; [summary] 4.4.1):
+# the input projection reads only the kept rows of the hidden states, and the output
+# projection's result is added into the residual stream at the kept rows only.
+# ----------------------------------------------------------------------------------------
+
+def proj_gather(x, w, kept, block: int) -> np.ndarray:
+    """y[b, r] = x[b, pos(r)] @ w^T for the kept ranks r of each batch row (compact output).
+
+    x: [B, S, K]; w: [N, K] (a linear layer's weight, out_features x in_features).
+    Returns float64 [B, max_r, N]; rows past a batch row's own kept count stay 0."""
+    x, w = _f64(x), _f64(w)
+    B = x.shape[0]
+    keptb = _per_batch(kept, B)
+    nmax = max(len(kb) for kb in keptb) * block
+    y = np.zeros((B, nmax, w.shape[0]))
+    for b in range(B):
+        pos = token_positions(keptb[b], block)
+        if len(pos):
+            y[b, :len(pos)] = x[b, pos] @ w.T
+    return y
+
+
+def proj_scatter_add(resid, y, w, kept, block: int) -> np.ndarray:
+    """resid[b, pos(r)] + y[b, r] @ w^T at the kept positions; every other row unchanged.
+
+    resid: [B, S, N]; y: [B, >= Nk, K] compact by kept rank; w: [N, K]."""
+    out = _f64(resid).copy()
+    y, w = _f64(y), _f64(w)
+    keptb = _per_batch(kept, out.shape[0])
+    for b in range(out.shape[0]):
+        pos = token_positions(keptb[b], block)
+        if len(pos):
+            out[b, pos] += y[b, :len(pos)] @ w.T
+    return out
+
+
+# ----------------------------------------------------------------------------------------
 # Selection ([notes] 4.2 layer-specific threshold, Algorithm 1 step 1; top-k by keep ratio)
 # ----------------------------------------------------------------------------------------
 
