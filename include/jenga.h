@@ -204,13 +204,56 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
                                     void* stream);
 
 /*
+ * Permutation-free token movement around the projections ([notes] §4.4; [summary] 4.4.1: the
+ * kept tokens are loaded straight from the full hidden-state tensor by the layer that consumes
+ * them, and the result is added into the residual stream in place -- no gathered copy, padding
+ * or separate residual pass).  bf16 inputs and weights, fp32 accumulation.
+ *
+ *   in_features   K, a multiple of 64;  out_features  N, a multiple of 128
+ *   in_stride     (batch, row) element strides of the input rows (16-byte aligned rows)
+ *   out_stride    (batch, row) element strides of the output rows
+ *   block         kept-block size (multiple of 64, <= 1024); seq_len % block == 0
+ */
+typedef struct {
+  int32_t batch, seq_len, block, in_features, out_features;
+  int64_t in_stride[2];
+  int64_t out_stride[2];
+} jenga_proj_problem;
+
+/*
+ * jenga_proj_gather — y[b][r][:] = x[b][pos(r)][:] . w^T for every kept rank r < Nk_b, where
+ * pos(r) = kept_idx[b][r / block] * block + r % block and Nk_b = min(n_kept[b],
+ * max_kept_blocks) * block.  Rows of y at or past Nk_b are not written.
+ *   x  [B][S][K] bf16 (full sequence; only kept rows are read)
+ *   w  [N][K] bf16, contiguous (a linear layer's weight)
+ *   y  [B][max_kept_blocks*block][N] bf16 (compact, by kept rank), written
+ * Errors: INVALID_ARG for null / misaligned pointers, bad strides or max_kept_blocks outside
+ * [1, nKB]; UNSUPPORTED for sizes outside the limits above or a row extent over 4 GiB.
+ */
+int jenga_proj_gather(const jenga_proj_problem* p, const void* x, const void* w,
+                      const int32_t* kept_idx, const int32_t* n_kept, int max_kept_blocks,
+                      void* y, void* stream);
+
+/*
+ * jenga_proj_scatter_add — resid[b][pos(r)][:] += y[b][r][:] . w^T for every kept rank r;
+ * rows of eliminated tokens are not touched.
+ *   y      [B][max_kept_blocks*block][K] bf16 (compact, by kept rank)
+ *   w      [N][K] bf16, contiguous
+ *   resid  [B][S][N] fp32, updated in place
+ * Errors as jenga_proj_gather.
+ */
+int jenga_proj_scatter_add(const jenga_proj_problem* p, const void* y, const void* w,
+                           const int32_t* kept_idx, const int32_t* n_kept, int max_kept_blocks,
+                           float* resid, void* stream);
+
+/*
  * Kernel timing (instrumentation; not part of the method).
  *
  * jenga_timing_enable(1) discards earlier records and, from then on, brackets every kernel
  * launched by the entry points above with two HIP events recorded on that call's stream;
  * jenga_timing_enable(0) stops recording (the records stay readable).  Kernel names:
  * k_slse64, k_smass64 (bf16 scoring), k_eq2_tiles, k_eq2_reduce (Eq. 2 scoring), k_select, k_pack_tp, k_fwd64, k_prep64, k_dkdv32,
- * k_dq64 (bf16 attention).  The fp32 kernels are not bracketed.
+ * k_dq64 (bf16 attention), k_proj_gather, k_proj_scatter.  The fp32 kernels are not bracketed.
  *
  * jenga_timing_query(kernel, launches, total_ms) waits for the recorded events of that name
  * and returns how many launches were recorded and the sum of their event-to-event times.

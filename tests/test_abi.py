@@ -155,3 +155,30 @@ def test_score_eq2_validation(J):
     assert f(pp=_problem(J, D=128, dtype=1, block=256)) == J.JENGA_ERR_UNSUPPORTED
     assert f(wsb=need - 1) == J.JENGA_ERR_WORKSPACE
     assert f(ws=0) == J.JENGA_ERR_WORKSPACE
+
+
+def test_proj_validation(J):
+    p = J.JengaProjProblem()
+    p.batch, p.seq_len, p.block, p.in_features, p.out_features = 1, 1024, 64, 256, 256
+    p.in_stride[0], p.in_stride[1] = 1024 * 256, 256
+    p.out_stride[0], p.out_stride[1] = 16 * 64 * 256, 256
+    g = lambda pp=p, maxk=4, x=FAKE: J.lib.jenga_proj_gather(ctypes.byref(pp), x, FAKE, FAKE, FAKE,
+                                                            maxk, FAKE, None)
+    assert g(maxk=0) == J.JENGA_ERR_INVALID_ARG
+    assert g(maxk=17) == J.JENGA_ERR_INVALID_ARG
+    assert g(x=0) == J.JENGA_ERR_INVALID_ARG
+    assert g(x=FAKE + 2) == J.JENGA_ERR_INVALID_ARG
+    bad = J.JengaProjProblem.from_buffer_copy(p)
+    bad.out_features = 192                                       # not a multiple of 128
+    assert g(pp=bad) == J.JENGA_ERR_UNSUPPORTED
+    bad = J.JengaProjProblem.from_buffer_copy(p)
+    bad.in_features = 96                                         # not a multiple of 64
+    assert g(pp=bad) == J.JENGA_ERR_UNSUPPORTED
+    bad = J.JengaProjProblem.from_buffer_copy(p)
+    bad.block = 32
+    assert g(pp=bad) == J.JENGA_ERR_UNSUPPORTED
+    bad = J.JengaProjProblem.from_buffer_copy(p)
+    bad.in_stride[1] = 257                                       # rows not 16-byte aligned
+    assert g(pp=bad) == J.JENGA_ERR_INVALID_ARG
+    assert J.lib.jenga_proj_scatter_add(None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None) == \
+        J.JENGA_ERR_INVALID_ARG

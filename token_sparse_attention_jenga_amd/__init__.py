@@ -31,8 +31,8 @@ JENGA_OP_SCORE_EQ2 = 3
 
 EXPORTED = ["jenga_status_string", "jenga_topk_count", "jenga_workspace_bytes",
             "jenga_score_blocks", "jenga_score_blocks_eq2", "jenga_select_blocks",
-            "jenga_sparse_attn_fwd", "jenga_sparse_attn_bwd_segmented", "jenga_timing_enable",
-            "jenga_timing_query"]
+            "jenga_sparse_attn_fwd", "jenga_sparse_attn_bwd_segmented", "jenga_proj_gather",
+            "jenga_proj_scatter_add", "jenga_timing_enable", "jenga_timing_query"]
 
 
 class JengaProblem(ctypes.Structure):
@@ -42,6 +42,12 @@ class JengaProblem(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
                 ("v_stride", ctypes.c_int64 * 3)]
+
+
+class JengaProjProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("in_features", ctypes.c_int32), ("out_features", ctypes.c_int32),
+                ("in_stride", ctypes.c_int64 * 2), ("out_stride", ctypes.c_int64 * 2)]
 
 
 class JengaError(RuntimeError):
@@ -74,6 +80,11 @@ def _load() -> ctypes.CDLL:
     lib.jenga_sparse_attn_bwd_segmented.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                                                     vp, i32, vp, sz, vp]
     lib.jenga_sparse_attn_bwd_segmented.restype = i32
+    PP = ctypes.POINTER(JengaProjProblem)
+    lib.jenga_proj_gather.argtypes = [PP, vp, vp, vp, vp, i32, vp, vp]
+    lib.jenga_proj_gather.restype = i32
+    lib.jenga_proj_scatter_add.argtypes = [PP, vp, vp, vp, vp, i32, vp, vp]
+    lib.jenga_proj_scatter_add.restype = i32
     lib.jenga_timing_enable.argtypes = [i32]
     lib.jenga_timing_enable.restype = i32
     lib.jenga_timing_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32),
@@ -269,3 +280,39 @@ def sparse_attn_bwd(q, k, v, kept_idx, n_kept, max_kept_blocks: int, block: int,
     jenga_sparse_attn_bwd_segmented(p, q, k, v, kept_idx, n_kept, max_kept_blocks, o_saved, lse,
                                     dout, dq, dk, dv, n_segments, ws)
     return dq, dk, dv
+
+
+# ------------------------------------------------------------------------------------------
+# permutation-free projections
+# ------------------------------------------------------------------------------------------
+
+def make_proj_problem(inp, w, out, block: int, seq_len: int) -> JengaProjProblem:
+    """inp: [B, rows, K] bf16 (rows = S for the gathered input, Ncap for compact rows);
+    w: [N, K] bf16; out: [B, rows_out, N] (bf16 compact or fp32 residual)."""
+    p = JengaProjProblem()
+    p.batch, p.seq_len, p.block = inp.shape[0], int(seq_len), int(block)
+    p.in_features, p.out_features = inp.shape[2], w.shape[0]
+    p.in_stride[0], p.in_stride[1] = inp.stride(0), inp.stride(1)
+    p.out_stride[0], p.out_stride[1] = out.stride(0), out.stride(1)
+    return p
+
+
+def proj_gather(x, w, kept_idx, n_kept, max_kept_blocks: int, block: int, stream=None):
+    """y[b, r] = x[b, pos(r)] @ w^T over the kept ranks (compact bf16 [B, Ncap, N])."""
+    import torch
+    B, S, _ = x.shape
+    y = torch.empty((B, max_kept_blocks * block, w.shape[0]), dtype=torch.bfloat16, device=x.device)
+    p = make_proj_problem(x, w, y, block, S)
+    st = lib.jenga_proj_gather(ctypes.byref(p), _ptr(x), _ptr(w), _ptr(kept_idx), _ptr(n_kept),
+                               int(max_kept_blocks), _ptr(y), _stream(stream))
+    _check("jenga_proj_gather", st)
+    return y
+
+
+def proj_scatter_add(y, w, kept_idx, n_kept, max_kept_blocks: int, block: int, resid,
+                     stream=None) -> None:
+    """resid[b, pos(r)] += y[b, r] @ w^T at the kept rows (resid fp32 [B, S, N], in place)."""
+    p = make_proj_problem(y, w, resid, block, resid.shape[1])
+    st = lib.jenga_proj_scatter_add(ctypes.byref(p), _ptr(y), _ptr(w), _ptr(kept_idx), _ptr(n_kept),
+                                    int(max_kept_blocks), _ptr(resid), _stream(stream))
+    _check("jenga_proj_scatter_add", st)

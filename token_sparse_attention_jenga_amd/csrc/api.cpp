@@ -100,6 +100,54 @@ size_t score_ws_bytes(const jenga_problem* p) {
   return align_up(lse) + align_up(mass);
 }
 
+int check_proj(const jenga_proj_problem* p, const void* in, const void* w, const int32_t* kept,
+               const int32_t* n_kept, int max_kept_blocks, const void* out, int out_es) {
+  if (!p || !in || !w || !kept || !n_kept || !out) return JENGA_ERR_INVALID_ARG;
+  if (p->batch <= 0 || p->seq_len <= 0 || p->block <= 0 || p->in_features <= 0 ||
+      p->out_features <= 0)
+    return JENGA_ERR_INVALID_ARG;
+  if (p->block % 64 != 0 || p->block > 1024 || p->seq_len % p->block != 0) return JENGA_ERR_UNSUPPORTED;
+  const int nkb = p->seq_len / p->block;
+  if (nkb > kMaxBlocks) return JENGA_ERR_UNSUPPORTED;
+  if (p->in_features % 64 != 0 || p->out_features % 128 != 0) return JENGA_ERR_UNSUPPORTED;
+  if (max_kept_blocks < 1 || max_kept_blocks > nkb) return JENGA_ERR_INVALID_ARG;
+  for (int i = 0; i < 2; ++i) {
+    if (p->in_stride[i] < 0 || (p->in_stride[i] * 2) % 16 != 0) return JENGA_ERR_INVALID_ARG;
+    if (p->out_stride[i] < 0 || (p->out_stride[i] * out_es) % 16 != 0) return JENGA_ERR_INVALID_ARG;
+  }
+  if (!aligned16(in) || !aligned16(w) || !aligned16(out)) return JENGA_ERR_INVALID_ARG;
+  // buffer-resource offsets are 32-bit: every per-batch-row extent stays below 4 GiB
+  const double lim = 4294967296.0;
+  if ((double)p->seq_len * (double)p->in_stride[1] * 2.0 >= lim) return JENGA_ERR_UNSUPPORTED;
+  if ((double)p->out_features * (double)p->in_features * 2.0 >= lim) return JENGA_ERR_UNSUPPORTED;
+  return JENGA_OK;
+}
+
+jenga::ProjParams proj_params(const jenga_proj_problem* p, const void* in, const void* w,
+                              const int32_t* kept, const int32_t* n_kept, int max_kept_blocks,
+                              void* out) {
+  jenga::ProjParams pp;
+  pp.a = in;
+  pp.as0 = p->in_stride[0];
+  pp.as1 = p->in_stride[1];
+  pp.w = w;
+  pp.out = out;
+  pp.os0 = p->out_stride[0];
+  pp.os1 = p->out_stride[1];
+  pp.kept = kept;
+  pp.n_kept = n_kept;
+  pp.B = p->batch;
+  pp.S = p->seq_len;
+  pp.K = p->in_features;
+  pp.N = p->out_features;
+  pp.block = p->block;
+  pp.nkb = p->seq_len / p->block;
+  pp.max_kept_blocks = max_kept_blocks;
+  pp.ncap = max_kept_blocks * p->block;
+  return pp;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -337,6 +385,25 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
     if (e != hipSuccess) return JENGA_ERR_LAUNCH;
   }
   return JENGA_OK;
+}
+
+
+int jenga_proj_gather(const jenga_proj_problem* p, const void* x, const void* w,
+                      const int32_t* kept_idx, const int32_t* n_kept, int max_kept_blocks,
+                      void* y, void* stream) {
+  const int st = check_proj(p, x, w, kept_idx, n_kept, max_kept_blocks, y, 2);
+  if (st != JENGA_OK) return st;
+  const jenga::ProjParams pp = proj_params(p, x, w, kept_idx, n_kept, max_kept_blocks, y);
+  return jenga::launch_proj(pp, true, (hipStream_t)stream) == hipSuccess ? JENGA_OK : JENGA_ERR_LAUNCH;
+}
+
+int jenga_proj_scatter_add(const jenga_proj_problem* p, const void* y, const void* w,
+                           const int32_t* kept_idx, const int32_t* n_kept, int max_kept_blocks,
+                           float* resid, void* stream) {
+  const int st = check_proj(p, y, w, kept_idx, n_kept, max_kept_blocks, resid, 4);
+  if (st != JENGA_OK) return st;
+  const jenga::ProjParams pp = proj_params(p, y, w, kept_idx, n_kept, max_kept_blocks, resid);
+  return jenga::launch_proj(pp, false, (hipStream_t)stream) == hipSuccess ? JENGA_OK : JENGA_ERR_LAUNCH;
 }
 
 int jenga_timing_enable(int enable) {

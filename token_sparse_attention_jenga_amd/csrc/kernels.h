@@ -27,6 +27,17 @@ struct Eq2Params {
   float* scores;      // [B][nkb]
 };
 
+struct ProjParams {
+  const void* a;        // bf16 input rows: gathered x [B][S][K] or compact y [B][Ncap][K]
+  int64_t as0, as1;     // element strides of a: batch, row
+  const void* w;        // bf16 [N][K], contiguous
+  void* out;            // bf16 compact [B][Ncap][N] (gather) or fp32 resid [B][S][N] (scatter)
+  int64_t os0, os1;     // element strides of out: batch, row
+  const int32_t* kept;
+  const int32_t* n_kept;
+  int B, S, K, N, block, nkb, max_kept_blocks, ncap;
+};
+
 struct SelectParams {
   const float* scores;
   int B, nkb, mode, kcount;
@@ -82,6 +93,9 @@ hipError_t launch_bwd_segment(const BwdParams& p, int dtype, int D, hipStream_t 
 
 // bf16 scoring with async LDS staging (score64.hip)
 hipError_t launch_score64(const ScoreParams& p, int D, hipStream_t st);
+
+// permutation-free projections (proj.hip): gathered input rows, or scatter-add into resid
+hipError_t launch_proj(const ProjParams& p, bool gather, hipStream_t st);
 
 // bf16 Eq. 2 literal scoring (eq2.hip): block 64 or 128
 hipError_t launch_score_eq2(const Eq2Params& p, int D, int block, hipStream_t st);
