@@ -201,6 +201,31 @@ def proj_scatter_add(resid, y, w, kept, block: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------
+# Loss of the language-model head, the step that segment-based peak cutting targets
+# ([summary] 4.4.2; [notes] 4.4): cross-entropy of softmax(h W^T) against the next tokens.
+# ----------------------------------------------------------------------------------------
+
+def lm_head_ce(h, w, targets):
+    """Mean cross-entropy over the T rows of h and its gradient with respect to h.
+
+    h: [T, d]; w: [V, d] (the head's weight); targets: [T] ints in [0, V).
+    logits = h w^T; row_loss_t = logsumexp(logits_t) - logits_t[target_t];
+    loss = mean_t row_loss_t; dh = ((softmax(logits) - onehot(targets)) / T) w.
+    Returns (loss, row_loss [T], dh [T, d]) in float64."""
+    h, w = _f64(h), _f64(w)
+    T = h.shape[0]
+    logits = h @ w.T
+    mx = logits.max(axis=1, keepdims=True)
+    lse = (mx + np.log(np.exp(logits - mx).sum(axis=1, keepdims=True)))[:, 0]
+    t = np.asarray(targets, dtype=np.int64)
+    row_loss = lse - logits[np.arange(T), t]
+    g = np.exp(logits - lse[:, None])
+    g[np.arange(T), t] -= 1.0
+    dh = (g / T) @ w
+    return float(row_loss.mean()), row_loss, dh
+
+
+# ----------------------------------------------------------------------------------------
 # Selection ([notes] 4.2 layer-specific threshold, Algorithm 1 step 1; top-k by keep ratio)
 # ----------------------------------------------------------------------------------------
 
