@@ -29,7 +29,8 @@ if ROOT not in sys.path:
 BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 bf16 flop/clk/CU x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
 KERNELS = ("k_slse64", "k_smass64", "k_eq2_tiles", "k_eq2_reduce", "k_select", "k_pack_tp",
-           "k_fwd64", "k_prep64", "k_dkdv32", "k_dq64", "k_proj_gather", "k_proj_scatter")
+           "k_fwd64", "k_prep64", "k_dkdv32", "k_dq64", "k_proj_gather", "k_proj_scatter",
+           "k_proj_logits", "k_ce_rows", "k_proj_dh")
 METRIC = "fwd+bwd token-sparse attn TFLOP/s (kept FLOPs) & tokens/s at S=32K; % MFMA peak"
 
 
@@ -373,6 +374,36 @@ def main():
                                             ((g_ms + s_ms) * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)}
         del xh, wqkv, wo, yo
 
+    # Segment-based peak cutting of the language-model-head loss (NEXT row): the head of this
+    # workload's d_model over its B*S tokens and a 32000-entry vocabulary, seeded synthetic
+    # bf16 weights and targets, in 1 and in 8 segments: time and the transient (workspace) bytes.
+    loss_seg = None
+    if cfg.dtype == "bf16" and (Hq * D) % 128 == 0 and (B * S) % 256 == 0:
+        dm, V, T = Hq * D, 32000, B * S
+        gen = torch.Generator(device=dev).manual_seed(777)
+        hh = torch.randn((T, dm), generator=gen, device=dev).to(torch.bfloat16)
+        wv = (torch.randn((V, dm), generator=gen, device=dev) / dm ** 0.5).to(torch.bfloat16)
+        wvt = wv.t().contiguous()
+        tg = torch.randint(0, V, (T,), generator=gen, device=dev, dtype=torch.int32)
+        loss_seg = {"tokens": T, "d_model": dm, "vocab": V}
+        for nseg_l in (1, 8):
+            pl = J.loss_problem(T, dm, V, nseg_l)
+            ws_l = J.alloc_workspace(J.loss_workspace_bytes(pl), dev)
+            J.lm_head_ce(hh, wv, wvt, tg, nseg_l, ws_l)                  # warm-up
+            torch.cuda.synchronize()
+            l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            l0.record(stream)
+            for _ in range(K):
+                J.lm_head_ce(hh, wv, wvt, tg, nseg_l, ws_l)
+            l1.record(stream)
+            torch.cuda.synchronize()
+            ms = l0.elapsed_time(l1) / K
+            loss_seg[f"segments_{nseg_l}"] = {
+                "ms": round(ms, 3), "tflops": round(4.0 * T * dm * V / (ms * 1e-3) / 1e12, 2),
+                "transient_mib": round(J.loss_workspace_bytes(pl) / 2**20, 1)}
+            del ws_l
+        del hh, wv, wvt, tg
+
     copy_ms = None
     if args.copy_calibration:
         # plain elementwise copy (16-byte vector loads/stores), 1 GiB read + 1 GiB written
@@ -426,6 +457,7 @@ def main():
         "kept_tokens_per_layer": nks,
         "eq2_scoring": eq2,
         "proj_fused": proj,
+        "loss_segmented": loss_seg,
         "roofline": roofline,
         "kernel_avg_us": kernel_avg_us,
         "cpu_baseline": cpu,

@@ -247,13 +247,50 @@ int jenga_proj_scatter_add(const jenga_proj_problem* p, const void* y, const voi
                            float* resid, void* stream);
 
 /*
+ * Segment-based peak cutting of the language-model-head loss ([summary] 4.4.2; [notes] §4.4:
+ * the loss step's transient -- logits over the whole vocabulary for every token -- is split
+ * into segments processed one after another, each segment's activations discarded before the
+ * next, so the transient peak follows tokens / n_segments).
+ *
+ *   tokens      T, a multiple of 32;   d_model  d, a multiple of 128
+ *   vocab       V, a multiple of 128, at most 32768;   n_segments in [1, T / 32]
+ * Segment rows L = ceil(T / n_segments) rounded up to 32 (the last segment may be shorter).
+ */
+typedef struct {
+  int32_t tokens, d_model, vocab, n_segments;
+} jenga_loss_problem;
+
+/* Workspace for one segment: L * V * (4 + 2) bytes (fp32 logits, bf16 logit gradient), rounded
+ * up to 256; 0 for an invalid problem.  This is the transient that segmenting bounds. */
+size_t jenga_loss_workspace_bytes(const jenga_loss_problem* p);
+
+/*
+ * jenga_lm_head_ce_segmented — mean next-token cross-entropy of the head logits = h w^T and its
+ * gradient with respect to h, one segment of L rows at a time:
+ *   row_loss[t] = logsumexp(logits_t) - logits_t[targets[t]]      (fp32, from fp32 logits)
+ *   loss[0]     = mean_t row_loss[t]                               (fp64 sum, fixed order)
+ *   dh[t][:]    = ((softmax(logits_t) - onehot(targets[t])) / T) w   (the factor in bf16)
+ *   h        [T][d] bf16 row-major        w  [V][d] bf16 (the head's weight)
+ *   wt       [d][V] bf16 (the same weight transposed, prepared once: the head is frozen)
+ *   targets  [T] int32 in [0, V)           row_loss [T] fp32, loss [1] fp32, dh [T][d] fp32
+ *   workspace >= jenga_loss_workspace_bytes(p), 256-byte aligned
+ * The results do not depend on n_segments.  Errors: INVALID_ARG (null / misaligned pointers),
+ * UNSUPPORTED (sizes outside the limits), WORKSPACE, LAUNCH.
+ */
+int jenga_lm_head_ce_segmented(const jenga_loss_problem* p, const void* h, const void* w,
+                               const void* wt, const int32_t* targets, float* row_loss,
+                               float* loss, float* dh, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * Kernel timing (instrumentation; not part of the method).
  *
  * jenga_timing_enable(1) discards earlier records and, from then on, brackets every kernel
  * launched by the entry points above with two HIP events recorded on that call's stream;
  * jenga_timing_enable(0) stops recording (the records stay readable).  Kernel names:
  * k_slse64, k_smass64 (bf16 scoring), k_eq2_tiles, k_eq2_reduce (Eq. 2 scoring), k_select, k_pack_tp, k_fwd64, k_prep64, k_dkdv32,
- * k_dq64 (bf16 attention), k_proj_gather, k_proj_scatter.  The fp32 kernels are not bracketed.
+ * k_dq64 (bf16 attention), k_proj_gather, k_proj_scatter, k_proj_logits, k_ce_rows, k_proj_dh
+ * (loss).  The fp32 kernels are not bracketed.
  *
  * jenga_timing_query(kernel, launches, total_ms) waits for the recorded events of that name
  * and returns how many launches were recorded and the sum of their event-to-event times.

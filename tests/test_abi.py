@@ -182,3 +182,18 @@ def test_proj_validation(J):
     assert g(pp=bad) == J.JENGA_ERR_INVALID_ARG
     assert J.lib.jenga_proj_scatter_add(None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None) == \
         J.JENGA_ERR_INVALID_ARG
+
+
+def test_loss_validation_and_workspace(J):
+    p1 = J.loss_problem(32768, 4096, 32000, 1)
+    p8 = J.loss_problem(32768, 4096, 32000, 8)
+    w1, w8 = J.loss_workspace_bytes(p1), J.loss_workspace_bytes(p8)
+    assert w1 == 32768 * 32000 * 6 and w8 == 4096 * 32000 * 6    # the transient scales as 1/N
+    assert J.loss_workspace_bytes(J.loss_problem(100, 4096, 32000, 1)) == 0   # tokens % 32
+    assert J.loss_workspace_bytes(J.loss_problem(64, 4096, 40000, 1)) == 0    # vocab > 32768
+    f = lambda pp=p8, ws=FAKE, wsb=w8, h=FAKE: J.lib.jenga_lm_head_ce_segmented(
+        ctypes.byref(pp), h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert f(h=0) == J.JENGA_ERR_INVALID_ARG
+    assert f(wsb=w8 - 1) == J.JENGA_ERR_WORKSPACE
+    assert f(pp=J.loss_problem(64, 4096, 32000, 3)) == J.JENGA_ERR_INVALID_ARG   # > T/32 segments
+    assert f(pp=J.loss_problem(64, 4000, 32000, 1)) == J.JENGA_ERR_UNSUPPORTED

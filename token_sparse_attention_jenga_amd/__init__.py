@@ -32,7 +32,8 @@ JENGA_OP_SCORE_EQ2 = 3
 EXPORTED = ["jenga_status_string", "jenga_topk_count", "jenga_workspace_bytes",
             "jenga_score_blocks", "jenga_score_blocks_eq2", "jenga_select_blocks",
             "jenga_sparse_attn_fwd", "jenga_sparse_attn_bwd_segmented", "jenga_proj_gather",
-            "jenga_proj_scatter_add", "jenga_timing_enable", "jenga_timing_query"]
+            "jenga_proj_scatter_add", "jenga_loss_workspace_bytes", "jenga_lm_head_ce_segmented",
+            "jenga_timing_enable", "jenga_timing_query"]
 
 
 class JengaProblem(ctypes.Structure):
@@ -48,6 +49,11 @@ class JengaProjProblem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("in_features", ctypes.c_int32), ("out_features", ctypes.c_int32),
                 ("in_stride", ctypes.c_int64 * 2), ("out_stride", ctypes.c_int64 * 2)]
+
+
+class JengaLossProblem(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int32), ("d_model", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("n_segments", ctypes.c_int32)]
 
 
 class JengaError(RuntimeError):
@@ -85,6 +91,11 @@ def _load() -> ctypes.CDLL:
     lib.jenga_proj_gather.restype = i32
     lib.jenga_proj_scatter_add.argtypes = [PP, vp, vp, vp, vp, i32, vp, vp]
     lib.jenga_proj_scatter_add.restype = i32
+    LP = ctypes.POINTER(JengaLossProblem)
+    lib.jenga_loss_workspace_bytes.argtypes = [LP]
+    lib.jenga_loss_workspace_bytes.restype = sz
+    lib.jenga_lm_head_ce_segmented.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.jenga_lm_head_ce_segmented.restype = i32
     lib.jenga_timing_enable.argtypes = [i32]
     lib.jenga_timing_enable.restype = i32
     lib.jenga_timing_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32),
@@ -316,3 +327,35 @@ def proj_scatter_add(y, w, kept_idx, n_kept, max_kept_blocks: int, block: int, r
     st = lib.jenga_proj_scatter_add(ctypes.byref(p), _ptr(y), _ptr(w), _ptr(kept_idx), _ptr(n_kept),
                                     int(max_kept_blocks), _ptr(resid), _stream(stream))
     _check("jenga_proj_scatter_add", st)
+
+
+# ------------------------------------------------------------------------------------------
+# segmented language-model-head loss
+# ------------------------------------------------------------------------------------------
+
+def loss_problem(tokens: int, d_model: int, vocab: int, n_segments: int) -> JengaLossProblem:
+    p = JengaLossProblem()
+    p.tokens, p.d_model, p.vocab, p.n_segments = tokens, d_model, vocab, n_segments
+    return p
+
+
+def loss_workspace_bytes(p: JengaLossProblem) -> int:
+    return int(lib.jenga_loss_workspace_bytes(ctypes.byref(p)))
+
+
+def lm_head_ce(h, w, wt, targets, n_segments: int = 1, workspace=None, stream=None):
+    """(loss [1] fp32, row_loss [T] fp32, dh [T, d] fp32) of the head logits h w^T, computed
+    n_segments rows-segments at a time.  wt is w transposed ([d, V], contiguous)."""
+    import torch
+    T, d = h.shape
+    V = w.shape[0]
+    p = loss_problem(T, d, V, n_segments)
+    ws = workspace if workspace is not None else alloc_workspace(loss_workspace_bytes(p), h.device)
+    row_loss = torch.empty((T,), dtype=torch.float32, device=h.device)
+    loss = torch.empty((1,), dtype=torch.float32, device=h.device)
+    dh = torch.empty((T, d), dtype=torch.float32, device=h.device)
+    st = lib.jenga_lm_head_ce_segmented(ctypes.byref(p), _ptr(h), _ptr(w), _ptr(wt), _ptr(targets),
+                                        _ptr(row_loss), _ptr(loss), _ptr(dh), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream))
+    _check("jenga_lm_head_ce_segmented", st)
+    return loss, row_loss, dh

@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libjenga.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn64.hip", "score.hip", "score64.hip", "eq2.hip", "proj.hip", "select.hip", "timing.cpp", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn64.hip", "score.hip", "score64.hip", "eq2.hip", "proj.hip", "loss.hip", "select.hip", "timing.cpp", "api.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall", "-Wno-unused-function"]

@@ -144,9 +144,34 @@ jenga::ProjParams proj_params(const jenga_proj_problem* p, const void* in, const
   pp.nkb = p->seq_len / p->block;
   pp.max_kept_blocks = max_kept_blocks;
   pp.ncap = max_kept_blocks * p->block;
+  pp.rows = 0;
   return pp;
 }
 
+
+int loss_rows(const jenga_loss_problem* p) {
+  int L = (p->tokens + p->n_segments - 1) / p->n_segments;
+  return (L + 31) / 32 * 32;
+}
+
+int check_loss(const jenga_loss_problem* p) {
+  if (!p) return JENGA_ERR_INVALID_ARG;
+  if (p->tokens <= 0 || p->d_model <= 0 || p->vocab <= 0 || p->n_segments <= 0)
+    return JENGA_ERR_INVALID_ARG;
+  if (p->tokens % 32 != 0 || p->d_model % 128 != 0 || p->vocab % 128 != 0 || p->vocab > 32768)
+    return JENGA_ERR_UNSUPPORTED;
+  if (p->n_segments > p->tokens / 32) return JENGA_ERR_INVALID_ARG;
+  const double lim = 4294967296.0;
+  if ((double)p->tokens * p->d_model * 2.0 >= lim || (double)p->vocab * p->d_model * 2.0 >= lim ||
+      (double)loss_rows(p) * p->vocab * 2.0 >= lim)
+    return JENGA_ERR_UNSUPPORTED;
+  return JENGA_OK;
+}
+
+size_t loss_ws_bytes(const jenga_loss_problem* p) {
+  const size_t L = loss_rows(p), V = p->vocab;
+  return align_up(L * V * sizeof(float)) + align_up(L * V * 2);
+}
 
 }  // namespace
 
@@ -394,7 +419,8 @@ int jenga_proj_gather(const jenga_proj_problem* p, const void* x, const void* w,
   const int st = check_proj(p, x, w, kept_idx, n_kept, max_kept_blocks, y, 2);
   if (st != JENGA_OK) return st;
   const jenga::ProjParams pp = proj_params(p, x, w, kept_idx, n_kept, max_kept_blocks, y);
-  return jenga::launch_proj(pp, true, (hipStream_t)stream) == hipSuccess ? JENGA_OK : JENGA_ERR_LAUNCH;
+  return jenga::launch_proj(pp, jenga::kGather, "k_proj_gather", (hipStream_t)stream) == hipSuccess
+             ? JENGA_OK : JENGA_ERR_LAUNCH;
 }
 
 int jenga_proj_scatter_add(const jenga_proj_problem* p, const void* y, const void* w,
@@ -403,7 +429,67 @@ int jenga_proj_scatter_add(const jenga_proj_problem* p, const void* y, const voi
   const int st = check_proj(p, y, w, kept_idx, n_kept, max_kept_blocks, resid, 4);
   if (st != JENGA_OK) return st;
   const jenga::ProjParams pp = proj_params(p, y, w, kept_idx, n_kept, max_kept_blocks, resid);
-  return jenga::launch_proj(pp, false, (hipStream_t)stream) == hipSuccess ? JENGA_OK : JENGA_ERR_LAUNCH;
+  return jenga::launch_proj(pp, jenga::kScatter, "k_proj_scatter", (hipStream_t)stream) == hipSuccess
+             ? JENGA_OK : JENGA_ERR_LAUNCH;
+}
+
+size_t jenga_loss_workspace_bytes(const jenga_loss_problem* p) {
+  if (check_loss(p) != JENGA_OK) return 0;
+  return loss_ws_bytes(p);
+}
+
+int jenga_lm_head_ce_segmented(const jenga_loss_problem* p, const void* h, const void* w,
+                               const void* wt, const int32_t* targets, float* row_loss,
+                               float* loss, float* dh, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const int st0 = check_loss(p);
+  if (st0 != JENGA_OK) return st0;
+  if (!h || !w || !wt || !targets || !row_loss || !loss || !dh) return JENGA_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w) || !aligned16(wt) || !aligned16(dh)) return JENGA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < loss_ws_bytes(p) || ((uintptr_t)workspace % kAlign) != 0)
+    return JENGA_ERR_WORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  const int T = p->tokens, d = p->d_model, V = p->vocab, L = loss_rows(p);
+  float* logits = (float*)workspace;
+  void* glog = (char*)workspace + align_up((size_t)L * V * sizeof(float));
+  for (int seg = 0; seg < p->n_segments; ++seg) {
+    const int r0 = seg * L;
+    const int rows = r0 < T ? (T - r0 < L ? T - r0 : L) : 0;
+    if (rows <= 0) break;
+    jenga::ProjParams g1{};                                   // logits = h_seg w^T
+    g1.a = (const char*)h + (size_t)r0 * d * 2;
+    g1.as1 = d;
+    g1.w = w;
+    g1.out = logits;
+    g1.os1 = V;
+    g1.B = 1;
+    g1.K = d;
+    g1.N = V;
+    g1.rows = rows;
+    if (jenga::launch_proj(g1, jenga::kPlain, "k_proj_logits", s) != hipSuccess) return JENGA_ERR_LAUNCH;
+    jenga::CeParams ce;
+    ce.logits = logits;
+    ce.targets = targets + r0;
+    ce.row_loss = row_loss + r0;
+    ce.dlogits = glog;
+    ce.rows = rows;
+    ce.V = V;
+    ce.grad_scale = 1.0f / (float)T;
+    if (jenga::launch_ce_rows(ce, s) != hipSuccess) return JENGA_ERR_LAUNCH;
+    jenga::ProjParams g2{};                                   // dh_seg = g w  (w^T rows)
+    g2.a = glog;
+    g2.as1 = V;
+    g2.w = wt;
+    g2.out = dh + (size_t)r0 * d;
+    g2.os1 = d;
+    g2.B = 1;
+    g2.K = V;
+    g2.N = d;
+    g2.rows = rows;
+    if (jenga::launch_proj(g2, jenga::kPlain, "k_proj_dh", s) != hipSuccess) return JENGA_ERR_LAUNCH;
+  }
+  if (jenga::launch_loss_mean(row_loss, T, loss, s) != hipSuccess) return JENGA_ERR_LAUNCH;
+  return JENGA_OK;
 }
 
 int jenga_timing_enable(int enable) {

@@ -27,6 +27,8 @@ struct Eq2Params {
   float* scores;      // [B][nkb]
 };
 
+enum ProjMode { kGather = 0, kScatter = 1, kPlain = 2 };
+
 struct ProjParams {
   const void* a;        // bf16 input rows: gathered x [B][S][K] or compact y [B][Ncap][K]
   int64_t as0, as1;     // element strides of a: batch, row
@@ -36,6 +38,16 @@ struct ProjParams {
   const int32_t* kept;
   const int32_t* n_kept;
   int B, S, K, N, block, nkb, max_kept_blocks, ncap;
+  int rows;             // plain mode: rows of a (a multiple of 32)
+};
+
+struct CeParams {
+  const float* logits;  // [rows][V] fp32
+  const int32_t* targets;  // [rows]
+  float* row_loss;      // [rows]
+  void* dlogits;        // bf16 [rows][V]: (softmax - onehot) * grad_scale
+  int rows, V;
+  float grad_scale;     // 1 / total rows of the mean
 };
 
 struct SelectParams {
@@ -94,8 +106,12 @@ hipError_t launch_bwd_segment(const BwdParams& p, int dtype, int D, hipStream_t 
 // bf16 scoring with async LDS staging (score64.hip)
 hipError_t launch_score64(const ScoreParams& p, int D, hipStream_t st);
 
-// permutation-free projections (proj.hip): gathered input rows, or scatter-add into resid
-hipError_t launch_proj(const ProjParams& p, bool gather, hipStream_t st);
+// projections (proj.hip): gathered input rows, scatter-add into resid, or plain rows
+hipError_t launch_proj(const ProjParams& p, int mode, const char* name, hipStream_t st);
+
+// language-model-head loss (loss.hip)
+hipError_t launch_ce_rows(const CeParams& p, hipStream_t st);
+hipError_t launch_loss_mean(const float* row_loss, int rows, float* loss, hipStream_t st);
 
 // bf16 Eq. 2 literal scoring (eq2.hip): block 64 or 128
 hipError_t launch_score_eq2(const Eq2Params& p, int D, int block, hipStream_t st);

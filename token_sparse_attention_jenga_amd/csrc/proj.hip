@@ -5,8 +5,9 @@
 // output is added into the residual stream in place, so no gathered copy, padding or separate
 // residual pass exists.
 //
-//   k_proj<true>   y[b][r][:]      = x[b][pos(r)][:] . W^T     gathered rows in, compact rows out (bf16)
-//   k_proj<false>  resid[b][pos(r)][:] += y[b][r][:] . W^T     compact rows in, residual updated in place
+//   k_proj<kGather>   y[b][r][:]          = x[b][pos(r)][:] . W^T   gathered rows in, compact rows out (bf16)
+//   k_proj<kScatter>  resid[b][pos(r)][:] += y[b][r][:] . W^T      compact rows in, residual updated in place
+//   k_proj<kPlain>    out[r][:]           = a[r][:] . W^T          contiguous rows (fp32 out), r < rows
 // pos(r) is the token position of kept rank r (kept-block list); W is [N][K] (out x in features).
 //
 // Workgroup: a 256 (rows) x 128 (output columns) tile, 8 waves of 64 x 64 (2 x 2 MFMA blocks).
@@ -19,8 +20,9 @@
 
 namespace jenga {
 
-template <bool GATHER>
+template <int MODE>
 __global__ __launch_bounds__(512, 1) void k_proj(ProjParams p) {
+  constexpr bool GATHER = MODE == kGather, PLAIN = MODE == kPlain;
   using C = T64<64>;                                      // one reduction chunk: 32 x 64 tiles
   constexpr int NW = 8, TM = 256, TN = 128;
   constexpr int AT = TM / 32, BT = TN / 32;               // 8 A tiles, 4 W tiles per chunk
@@ -34,11 +36,11 @@ __global__ __launch_bounds__(512, 1) void k_proj(ProjParams p) {
 
   const Tile3 tl = xcd_tile();
   const int mt = tl.x, nt = tl.y, b = tl.z;
-  const int32_t* kept = p.kept + (int64_t)b * p.nkb;
-  const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
+  const int32_t* kept = PLAIN ? nullptr : p.kept + (int64_t)b * p.nkb;
+  const int Nk = PLAIN ? p.rows : min(p.n_kept[b], p.max_kept_blocks) * p.block;
   const int r0 = mt * TM, n0 = nt * TN;
   if (r0 >= Nk) return;
-  stage_kept(ktab, kept, (min(r0 + TM, Nk) - 1) / p.block + 1);
+  if (!PLAIN) stage_kept(ktab, kept, (min(r0 + TM, Nk) - 1) / p.block + 1);
   __syncthreads();
   const KeptTab kt{(const LDS_AS int*)ktab, kept, p.block};
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
@@ -57,6 +59,7 @@ __global__ __launch_bounds__(512, 1) void k_proj(ProjParams p) {
   const rsrc_t rw = make_rsrc(p.w);
   // first row of A tile t (rows past the kept count load a harmless valid row instead, so
   // that every wave issues the same number of loads per chunk)
+  // (the row count is a multiple of 32 in every mode, so a 32-row group is whole or past it)
   auto arow0 = [&](int t) -> int64_t {
     const int r = r0 + 32 * t < Nk ? r0 + 32 * t : 0;
     return GATHER ? kt.pos_u(r) : r;
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(512, 1) void k_proj(ProjParams p) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int rb = r0 + 64 * wm + 32 * mb;
-    if (rb >= Nk) continue;                                // Nk is a multiple of 64
+    if (rb >= Nk) continue;                                // Nk is a multiple of 32
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg)
 #pragma unroll
@@ -137,6 +140,9 @@ __global__ __launch_bounds__(512, 1) void k_proj(ProjParams p) {
           if (GATHER) {
             bf16* orow = (bf16*)p.out + b * p.os0 + (int64_t)r * p.os1;
             orow[col] = (bf16)v;
+          } else if (PLAIN) {
+            float* orow = (float*)p.out + b * p.os0 + (int64_t)r * p.os1;
+            orow[col] = v;
           } else {
             float* orow = (float*)p.out + b * p.os0 + (int64_t)kt.pos(r) * p.os1;
             orow[col] += v;
@@ -146,15 +152,18 @@ __global__ __launch_bounds__(512, 1) void k_proj(ProjParams p) {
   }
 }
 
-template <bool GATHER>
-static hipError_t launch_proj_t(const ProjParams& p, hipStream_t st) {
-  TimedLaunch tl(GATHER ? "k_proj_gather" : "k_proj_scatter", st);
-  k_proj<GATHER><<<dim3((p.ncap + 255) / 256, p.N / 128, p.B), 512, 0, st>>>(p);
+template <int MODE>
+static hipError_t launch_proj_t(const ProjParams& p, const char* name, hipStream_t st) {
+  TimedLaunch tl(name, st);
+  const int rows = MODE == kPlain ? p.rows : p.ncap;
+  k_proj<MODE><<<dim3((rows + 255) / 256, p.N / 128, p.B), 512, 0, st>>>(p);
   return hipGetLastError();
 }
 
-hipError_t launch_proj(const ProjParams& p, bool gather, hipStream_t st) {
-  return gather ? launch_proj_t<true>(p, st) : launch_proj_t<false>(p, st);
+hipError_t launch_proj(const ProjParams& p, int mode, const char* name, hipStream_t st) {
+  if (mode == kGather) return launch_proj_t<kGather>(p, name, st);
+  if (mode == kScatter) return launch_proj_t<kScatter>(p, name, st);
+  return launch_proj_t<kPlain>(p, name, st);
 }
 
 }  // namespace jenga
