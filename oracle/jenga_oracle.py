@@ -226,6 +226,81 @@ def lm_head_ce(h, w, targets):
 
 
 # ----------------------------------------------------------------------------------------
+# Token elimination in the MLP block ([summary] 4.2.4; [notes] 4.2 "extend to MLP block"):
+# a token's informativeness comes from the block's intermediate activation -- the ReLU
+# output for ReLU MLPs, SiLU(gate) * up for gated SiLU MLPs.  Readings: a token's score is
+# the mean activation magnitude over the F intermediate units (the units stand where the
+# heads stand in Eq. 2; for ReLU every activation is >= 0, so this is Eq. 2's positive-part
+# mean); a token block's score is the maximum over its tokens (Eq. 2's block maximum); the
+# kept blocks then run the down projection, added into the residual in place.
+# ----------------------------------------------------------------------------------------
+
+MLP_RELU = 0
+MLP_SILU_GATED = 1
+
+
+def mlp_activation(x, w1, w_up=None, kind: int = MLP_SILU_GATED) -> np.ndarray:
+    """Intermediate activation of an MLP block.
+
+    x: [..., K]; w1: [F, K] (ReLU MLPs: the first linear layer; gated MLPs: the gate
+    projection); w_up: [F, K], the up projection of gated MLPs (unused for ReLU).
+    ReLU:       a = max(x w1^T, 0)
+    SiLU gated: a = silu(x w1^T) * (x w_up^T), silu(z) = z / (1 + exp(-z))."""
+    x, w1 = _f64(x), _f64(w1)
+    z = x @ w1.T
+    if kind == MLP_RELU:
+        return np.maximum(z, 0.0)
+    u = x @ _f64(w_up).T
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z)) * u
+
+
+def mlp_token_scores(act) -> np.ndarray:
+    """Per-token informativeness: mean over the F units of |a| (last axis)."""
+    act = _f64(act)
+    return np.abs(act).sum(axis=-1) / act.shape[-1]
+
+
+def mlp_block_scores(act, block: int) -> np.ndarray:
+    """Per-token-block informativeness: the maximum token score in each block of b tokens.
+
+    act: [B, S, F] -> [B, S / b]."""
+    e = mlp_token_scores(act)
+    B, S = e.shape
+    return e.reshape(B, S // block, block).max(axis=2)
+
+
+def proj_gather_scatter_add(resid, a, w, kept, block: int) -> np.ndarray:
+    """resid[b, pos(r)] + a[b, pos(r)] @ w^T at the kept positions; every other row unchanged.
+
+    resid: [B, S, N]; a: [B, S, K] (full rows, read only where kept); w: [N, K]."""
+    out = _f64(resid).copy()
+    a, w = _f64(a), _f64(w)
+    keptb = _per_batch(kept, out.shape[0])
+    for b in range(out.shape[0]):
+        pos = token_positions(keptb[b], block)
+        if len(pos):
+            out[b, pos] += a[b, pos] @ w.T
+    return out
+
+
+def mlp_sparse_forward(x, w1, w_up, w_down, resid, block: int, mode: int, param,
+                       kind: int = MLP_SILU_GATED, act_round=None):
+    """One MLP block with token elimination: activation for every token, block scores,
+    selection (the same rule as for attention), then the down projection of the kept
+    tokens only, added into the residual in place.
+
+    act_round: optional function applied to the activation before the down projection
+    (the stored precision of the activation, e.g. a bf16 rounding); the scores always come
+    from the unrounded activation.  Returns (resid_out, block_scores, kept per batch row)."""
+    act = mlp_activation(x, w1, w_up, kind)
+    sc = mlp_block_scores(act, block)
+    kept = [select_blocks(sc[b].astype(np.float32), mode, param) for b in range(sc.shape[0])]
+    a_down = act if act_round is None else _f64(act_round(act))
+    return proj_gather_scatter_add(resid, a_down, w_down, kept, block), sc, kept
+
+
+# ----------------------------------------------------------------------------------------
 # Selection ([notes] 4.2 layer-specific threshold, Algorithm 1 step 1; top-k by keep ratio)
 # ----------------------------------------------------------------------------------------
 
