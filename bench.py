@@ -30,7 +30,8 @@ BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 bf16 flop/clk/CU x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
 KERNELS = ("k_slse64", "k_smass64", "k_eq2_tiles", "k_eq2_reduce", "k_select", "k_pack_tp",
            "k_fwd64", "k_prep64", "k_dkdv32", "k_dq64", "k_proj_gather", "k_proj_scatter",
-           "k_proj_logits", "k_ce_rows", "k_proj_dh")
+           "k_proj_logits", "k_ce_rows", "k_proj_dh", "k_mlp_act_gated", "k_mlp_block",
+           "k_proj_gather_scatter")
 METRIC = "fwd+bwd token-sparse attn TFLOP/s (kept FLOPs) & tokens/s at S=32K; % MFMA peak"
 
 
@@ -374,6 +375,45 @@ def main():
                                             ((g_ms + s_ms) * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)}
         del xh, wqkv, wo, yo
 
+    # Token elimination in the MLP block (NEXT row): a Llama-2-7B-shaped gated SiLU MLP
+    # (d_model of this workload, 11008 units) over the B*S tokens with seeded synthetic bf16
+    # weights: activation + token/block informativeness, selection at this workload's keep
+    # rule, and the down projection of the kept tokens into the residual.
+    mlp = None
+    if cfg.dtype == "bf16" and (Hq * D) % 128 == 0:
+        dm, F = Hq * D, 11008
+        gen = torch.Generator(device=dev).manual_seed(99)
+        xm = torch.randn((B, S, dm), generator=gen, device=dev).to(torch.bfloat16)
+        wg = (torch.randn((F, dm), generator=gen, device=dev) / dm ** 0.5).to(torch.bfloat16)
+        wu = (torch.randn((F, dm), generator=gen, device=dev) / dm ** 0.5).to(torch.bfloat16)
+        wdn = (torch.randn((dm, F), generator=gen, device=dev) / F ** 0.5).to(torch.bfloat16)
+        res2 = resid.view(B, S, dm)
+        pm = J.make_proj_problem(xm, wg, xm.new_empty((B, S, F)), blk, S)
+        ws_m = J.alloc_workspace(J.mlp_workspace_bytes(pm, J.JENGA_MLP_SILU_GATED), dev)
+        J.sparse_mlp_forward(xm, wg, wu, wdn, res2, blk, mode, cfg.select_param, workspace=ws_m)
+        torch.cuda.synchronize()
+        J.timing_enable(True)
+        nk_m = []
+        for _ in range(K):
+            _, _, nkm, _ = J.sparse_mlp_forward(xm, wg, wu, wdn, res2, blk, mode, cfg.select_param,
+                                                workspace=ws_m)
+            nk_m.append(nkm)
+        J.timing_enable(False)
+        torch.cuda.synchronize()
+        kept_rows = float(torch.stack(nk_m).double().mean().item()) * blk * B
+        na, ta = J.timing_query("k_mlp_act_gated")
+        nb_, tb = J.timing_query("k_mlp_block")
+        nd_, td = J.timing_query("k_proj_gather_scatter")
+        a_ms, b_ms, d_ms = ta / max(na, 1), tb / max(nb_, 1), td / max(nd_, 1)
+        a_tf = 2.0 * B * S * dm * 2 * F / (a_ms * 1e-3) / 1e12
+        d_tf = 2.0 * kept_rows * F * dm / (d_ms * 1e-3) / 1e12
+        mlp = {"d_model": dm, "units": F, "tokens": B * S, "kept_rows": kept_rows,
+               "act_scores_ms": round(a_ms + b_ms, 4), "act_gemm_tflops": round(a_tf, 2),
+               "block_scores_ms": round(b_ms, 4),
+               "down_kept_ms": round(d_ms, 4), "down_kept_tflops": round(d_tf, 2),
+               "pct_bf16_mfma_peak_act": round(100 * a_tf / BF16_PEAK_TFLOPS, 2)}
+        del xm, wg, wu, wdn, ws_m
+
     # Segment-based peak cutting of the language-model-head loss (NEXT row): the head of this
     # workload's d_model over its B*S tokens and a 32000-entry vocabulary, seeded synthetic
     # bf16 weights and targets, in 1 and in 8 segments: time and the transient (workspace) bytes.
@@ -458,6 +498,7 @@ def main():
         "eq2_scoring": eq2,
         "proj_fused": proj,
         "loss_segmented": loss_seg,
+        "mlp_elimination": mlp,
         "roofline": roofline,
         "kernel_avg_us": kernel_avg_us,
         "cpu_baseline": cpu,

@@ -247,6 +247,54 @@ int jenga_proj_scatter_add(const jenga_proj_problem* p, const void* y, const voi
                            float* resid, void* stream);
 
 /*
+ * jenga_proj_gather_scatter_add — resid[b][pos(r)][:] += a[b][pos(r)][:] . w^T for every kept
+ * rank r; rows of eliminated tokens are neither read nor written.  The down projection of an
+ * MLP block with token elimination (aipaper summary §4.2.4 with the permutation-free movement
+ * of papercache notes §4.4).
+ *   a      [B][S][K] bf16 (full sequence, in_stride; only kept rows are read)
+ *   w      [N][K] bf16, contiguous
+ *   resid  [B][S][N] fp32 (out_stride), updated in place
+ * Errors as jenga_proj_gather.
+ */
+int jenga_proj_gather_scatter_add(const jenga_proj_problem* p, const void* a, const void* w,
+                                  const int32_t* kept_idx, const int32_t* n_kept,
+                                  int max_kept_blocks, float* resid, void* stream);
+
+/*
+ * Token elimination in the MLP block (aipaper summary §4.2.4; papercache notes §4.2): a token's
+ * informativeness comes from the block's intermediate activation.
+ *   JENGA_MLP_RELU        act = max(x w1^T, 0)                      (ReLU MLPs)
+ *   JENGA_MLP_SILU_GATED  act = silu(x w1^T) * (x w_up^T)           (gated SiLU MLPs; w1 = gate)
+ * Token score e[b][t] = mean over the F units of |act[b][t][:]| (from the fp32 activation,
+ * before its rounding to bf16); block score = max of e over the block's tokens.  Selection then
+ * uses jenga_select_blocks on the block scores; jenga_proj_gather_scatter_add runs the down
+ * projection of the kept tokens.
+ * The problem is a jenga_proj_problem: in_features = K (model width, multiple of 64),
+ * out_features = F (units: multiple of 64 gated, of 128 ReLU), in_stride for x, out_stride for
+ * act (both bf16 element strides).
+ */
+#define JENGA_MLP_RELU 0
+#define JENGA_MLP_SILU_GATED 1
+
+/* Workspace: B * (F / 32) * S * 4 bytes (partial |act| sums), rounded up to 256; 0 for an
+ * invalid problem or kind. */
+size_t jenga_mlp_workspace_bytes(const jenga_proj_problem* p, int kind);
+
+/*
+ * jenga_mlp_act_scores — activation and informativeness of every token.
+ *   x             [B][S][K] bf16        w1, w_up  [F][K] bf16 contiguous (w_up unused for ReLU)
+ *   act           [B][S][F] bf16, written        token_scores [B][S] fp32, written
+ *   block_scores  [B][S / block] fp32, written   workspace >= jenga_mlp_workspace_bytes, 256-aligned
+ * Token scores sum the per-unit magnitudes in a fixed order (fp32 groups of 32, then fp64),
+ * so results repeat bit for bit.  Errors: INVALID_ARG (null / misaligned pointers, bad
+ * strides, unknown kind), UNSUPPORTED (sizes outside the limits or a row extent over 4 GiB),
+ * WORKSPACE, LAUNCH.
+ */
+int jenga_mlp_act_scores(const jenga_proj_problem* p, int kind, const void* x, const void* w1,
+                         const void* w_up, void* act, float* token_scores, float* block_scores,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Segment-based peak cutting of the language-model-head loss ([summary] 4.4.2; [notes] §4.4:
  * the loss step's transient -- logits over the whole vocabulary for every token -- is split
  * into segments processed one after another, each segment's activations discarded before the
@@ -289,8 +337,9 @@ int jenga_lm_head_ce_segmented(const jenga_loss_problem* p, const void* h, const
  * launched by the entry points above with two HIP events recorded on that call's stream;
  * jenga_timing_enable(0) stops recording (the records stay readable).  Kernel names:
  * k_slse64, k_smass64 (bf16 scoring), k_eq2_tiles, k_eq2_reduce (Eq. 2 scoring), k_select, k_pack_tp, k_fwd64, k_prep64, k_dkdv32,
- * k_dq64 (bf16 attention), k_proj_gather, k_proj_scatter, k_proj_logits, k_ce_rows, k_proj_dh
- * (loss).  The fp32 kernels are not bracketed.
+ * k_dq64 (bf16 attention), k_proj_gather, k_proj_scatter, k_proj_gather_scatter,
+ * k_mlp_act_gated, k_mlp_act_relu, k_mlp_block (MLP elimination), k_proj_logits, k_ce_rows,
+ * k_proj_dh (loss).  The fp32 kernels are not bracketed.
  *
  * jenga_timing_query(kernel, launches, total_ms) waits for the recorded events of that name
  * and returns how many launches were recorded and the sum of their event-to-event times.

@@ -184,6 +184,39 @@ def test_proj_validation(J):
         J.JENGA_ERR_INVALID_ARG
 
 
+def test_mlp_validation_and_workspace(J):
+    p = J.JengaProjProblem()
+    p.batch, p.seq_len, p.block, p.in_features, p.out_features = 1, 32768, 128, 4096, 11008
+    p.in_stride[0], p.in_stride[1] = 32768 * 4096, 4096
+    p.out_stride[0], p.out_stride[1] = 32768 * 11008, 11008
+    gated, relu = J.JENGA_MLP_SILU_GATED, J.JENGA_MLP_RELU
+    wsb = J.mlp_workspace_bytes(p, gated)
+    assert wsb == 32768 * (11008 // 32) * 4                   # partial sums per 32 units
+    assert J.mlp_workspace_bytes(p, relu) == wsb                # 11008 = 86 * 128
+    p64 = J.JengaProjProblem.from_buffer_copy(p)
+    p64.out_features = 11072                                    # a multiple of 64, not of 128
+    assert J.mlp_workspace_bytes(p64, gated) > 0
+    assert J.mlp_workspace_bytes(p64, relu) == 0                # ReLU tiles need F % 128 == 0
+    assert J.mlp_workspace_bytes(p, 2) == 0                     # unknown kind
+    f = lambda pp=p, kind=gated, x=FAKE, wu=FAKE, ws=FAKE, n=wsb: J.lib.jenga_mlp_act_scores(
+        ctypes.byref(pp), kind, x, FAKE, wu, FAKE, FAKE, FAKE, ws, n, None)
+    assert f(kind=5) == J.JENGA_ERR_INVALID_ARG
+    assert f(x=0) == J.JENGA_ERR_INVALID_ARG
+    assert f(wu=0) == J.JENGA_ERR_INVALID_ARG                  # gated needs the up projection
+    assert f(x=FAKE + 2) == J.JENGA_ERR_INVALID_ARG
+    assert f(n=wsb - 1) == J.JENGA_ERR_WORKSPACE
+    assert f(ws=FAKE + 16) == J.JENGA_ERR_WORKSPACE             # not 256-byte aligned
+    assert f(pp=p64, kind=relu) == J.JENGA_ERR_UNSUPPORTED
+    bad = J.JengaProjProblem.from_buffer_copy(p)
+    bad.block = 96
+    assert f(pp=bad) == J.JENGA_ERR_UNSUPPORTED
+    bad = J.JengaProjProblem.from_buffer_copy(p)
+    bad.out_stride[1] = 11009                                  # act rows not 16-byte aligned
+    assert f(pp=bad) == J.JENGA_ERR_INVALID_ARG
+    assert J.lib.jenga_proj_gather_scatter_add(None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None) == \
+        J.JENGA_ERR_INVALID_ARG
+
+
 def test_loss_validation_and_workspace(J):
     p1 = J.loss_problem(32768, 4096, 32000, 1)
     p8 = J.loss_problem(32768, 4096, 32000, 8)

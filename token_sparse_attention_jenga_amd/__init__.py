@@ -23,6 +23,8 @@ JENGA_DTYPE_BF16 = 1
 JENGA_SELECT_TOPK = 0
 JENGA_SELECT_THRESH_REL = 1
 JENGA_SELECT_THRESH_ABS = 2
+JENGA_MLP_RELU = 0
+JENGA_MLP_SILU_GATED = 1
 JENGA_FORCE_FIRST_BLOCK = 1
 JENGA_OP_SCORE = 0
 JENGA_OP_FWD = 1
@@ -32,7 +34,8 @@ JENGA_OP_SCORE_EQ2 = 3
 EXPORTED = ["jenga_status_string", "jenga_topk_count", "jenga_workspace_bytes",
             "jenga_score_blocks", "jenga_score_blocks_eq2", "jenga_select_blocks",
             "jenga_sparse_attn_fwd", "jenga_sparse_attn_bwd_segmented", "jenga_proj_gather",
-            "jenga_proj_scatter_add", "jenga_loss_workspace_bytes", "jenga_lm_head_ce_segmented",
+            "jenga_proj_scatter_add", "jenga_proj_gather_scatter_add", "jenga_mlp_workspace_bytes",
+            "jenga_mlp_act_scores", "jenga_loss_workspace_bytes", "jenga_lm_head_ce_segmented",
             "jenga_timing_enable", "jenga_timing_query"]
 
 
@@ -91,6 +94,12 @@ def _load() -> ctypes.CDLL:
     lib.jenga_proj_gather.restype = i32
     lib.jenga_proj_scatter_add.argtypes = [PP, vp, vp, vp, vp, i32, vp, vp]
     lib.jenga_proj_scatter_add.restype = i32
+    lib.jenga_proj_gather_scatter_add.argtypes = [PP, vp, vp, vp, vp, i32, vp, vp]
+    lib.jenga_proj_gather_scatter_add.restype = i32
+    lib.jenga_mlp_workspace_bytes.argtypes = [PP, i32]
+    lib.jenga_mlp_workspace_bytes.restype = sz
+    lib.jenga_mlp_act_scores.argtypes = [PP, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.jenga_mlp_act_scores.restype = i32
     LP = ctypes.POINTER(JengaLossProblem)
     lib.jenga_loss_workspace_bytes.argtypes = [LP]
     lib.jenga_loss_workspace_bytes.restype = sz
@@ -327,6 +336,57 @@ def proj_scatter_add(y, w, kept_idx, n_kept, max_kept_blocks: int, block: int, r
     st = lib.jenga_proj_scatter_add(ctypes.byref(p), _ptr(y), _ptr(w), _ptr(kept_idx), _ptr(n_kept),
                                     int(max_kept_blocks), _ptr(resid), _stream(stream))
     _check("jenga_proj_scatter_add", st)
+
+
+def proj_gather_scatter_add(a, w, kept_idx, n_kept, max_kept_blocks: int, block: int, resid,
+                            stream=None) -> None:
+    """resid[b, pos(r)] += a[b, pos(r)] @ w^T at the kept rows (a bf16 [B, S, K] full rows,
+    resid fp32 [B, S, N], in place)."""
+    p = make_proj_problem(a, w, resid, block, resid.shape[1])
+    st = lib.jenga_proj_gather_scatter_add(ctypes.byref(p), _ptr(a), _ptr(w), _ptr(kept_idx),
+                                           _ptr(n_kept), int(max_kept_blocks), _ptr(resid),
+                                           _stream(stream))
+    _check("jenga_proj_gather_scatter_add", st)
+
+
+# ------------------------------------------------------------------------------------------
+# token elimination in the MLP block
+# ------------------------------------------------------------------------------------------
+
+def mlp_workspace_bytes(p: JengaProjProblem, kind: int) -> int:
+    return int(lib.jenga_mlp_workspace_bytes(ctypes.byref(p), int(kind)))
+
+
+def mlp_act_scores(x, w1, w_up, kind: int, block: int, workspace=None, stream=None):
+    """(act bf16 [B, S, F], token_scores fp32 [B, S], block_scores fp32 [B, S / block]).
+    x bf16 [B, S, K]; w1 (gate or first layer) and w_up bf16 [F, K] (w_up None for ReLU)."""
+    import torch
+    B, S, _ = x.shape
+    F = w1.shape[0]
+    act = torch.empty((B, S, F), dtype=torch.bfloat16, device=x.device)
+    tok = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    blk = torch.empty((B, S // block), dtype=torch.float32, device=x.device)
+    p = make_proj_problem(x, w1, act, block, S)
+    ws = workspace if workspace is not None else alloc_workspace(mlp_workspace_bytes(p, kind), x.device)
+    st = lib.jenga_mlp_act_scores(ctypes.byref(p), int(kind), _ptr(x), _ptr(w1),
+                                  _ptr(w_up) if w_up is not None else None, _ptr(act), _ptr(tok),
+                                  _ptr(blk), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream))
+    _check("jenga_mlp_act_scores", st)
+    return act, tok, blk
+
+
+def sparse_mlp_forward(x, w1, w_up, w_down, resid, block: int, mode: int, param: float,
+                       kind: int = JENGA_MLP_SILU_GATED, workspace=None):
+    """One MLP block with token elimination: activation and scores for every token, block
+    selection, then the down projection of the kept tokens added into resid (fp32, in place).
+    Returns (block_scores, kept_idx, n_kept, max_kept_blocks)."""
+    act, _, blk = mlp_act_scores(x, w1, w_up, kind, block, workspace)
+    nkb = blk.shape[1]
+    kept, n_kept = select_blocks(blk, block, x.shape[1], mode, param)
+    mkb = topk_count(param, nkb) if mode == JENGA_SELECT_TOPK else nkb
+    proj_gather_scatter_add(act, w_down, kept, n_kept, mkb, block, resid)
+    return blk, kept, n_kept, mkb
 
 
 # ------------------------------------------------------------------------------------------

@@ -173,6 +173,29 @@ size_t loss_ws_bytes(const jenga_loss_problem* p) {
   return align_up(L * V * sizeof(float)) + align_up(L * V * 2);
 }
 
+int check_mlp(const jenga_proj_problem* p, int kind) {
+  if (!p || (kind != JENGA_MLP_RELU && kind != JENGA_MLP_SILU_GATED)) return JENGA_ERR_INVALID_ARG;
+  if (p->batch <= 0 || p->seq_len <= 0 || p->block <= 0 || p->in_features <= 0 ||
+      p->out_features <= 0)
+    return JENGA_ERR_INVALID_ARG;
+  if (p->block % 64 != 0 || p->block > 1024 || p->seq_len % p->block != 0) return JENGA_ERR_UNSUPPORTED;
+  if (p->seq_len / p->block > kMaxBlocks) return JENGA_ERR_UNSUPPORTED;
+  if (p->in_features % 64 != 0) return JENGA_ERR_UNSUPPORTED;
+  if (p->out_features % (kind == JENGA_MLP_SILU_GATED ? 64 : 128) != 0) return JENGA_ERR_UNSUPPORTED;
+  for (int i = 0; i < 2; ++i)
+    if (p->in_stride[i] < 0 || p->out_stride[i] < 0 || (p->in_stride[i] * 2) % 16 != 0 ||
+        (p->out_stride[i] * 2) % 16 != 0)
+      return JENGA_ERR_INVALID_ARG;
+  const double lim = 4294967296.0;
+  if ((double)p->seq_len * (double)p->in_stride[1] * 2.0 >= lim) return JENGA_ERR_UNSUPPORTED;
+  if ((double)p->out_features * (double)p->in_features * 2.0 >= lim) return JENGA_ERR_UNSUPPORTED;
+  return JENGA_OK;
+}
+
+size_t mlp_ws_bytes(const jenga_proj_problem* p) {
+  return align_up((size_t)p->batch * (p->out_features / 32) * (size_t)p->seq_len * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -431,6 +454,67 @@ int jenga_proj_scatter_add(const jenga_proj_problem* p, const void* y, const voi
   const jenga::ProjParams pp = proj_params(p, y, w, kept_idx, n_kept, max_kept_blocks, resid);
   return jenga::launch_proj(pp, jenga::kScatter, "k_proj_scatter", (hipStream_t)stream) == hipSuccess
              ? JENGA_OK : JENGA_ERR_LAUNCH;
+}
+
+int jenga_proj_gather_scatter_add(const jenga_proj_problem* p, const void* a, const void* w,
+                                  const int32_t* kept_idx, const int32_t* n_kept,
+                                  int max_kept_blocks, float* resid, void* stream) {
+  const int st = check_proj(p, a, w, kept_idx, n_kept, max_kept_blocks, resid, 4);
+  if (st != JENGA_OK) return st;
+  const jenga::ProjParams pp = proj_params(p, a, w, kept_idx, n_kept, max_kept_blocks, resid);
+  return jenga::launch_proj(pp, jenga::kGatherScatter, "k_proj_gather_scatter",
+                            (hipStream_t)stream) == hipSuccess
+             ? JENGA_OK : JENGA_ERR_LAUNCH;
+}
+
+size_t jenga_mlp_workspace_bytes(const jenga_proj_problem* p, int kind) {
+  if (check_mlp(p, kind) != JENGA_OK) return 0;
+  return mlp_ws_bytes(p);
+}
+
+int jenga_mlp_act_scores(const jenga_proj_problem* p, int kind, const void* x, const void* w1,
+                         const void* w_up, void* act, float* token_scores, float* block_scores,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_mlp(p, kind);
+  if (st != JENGA_OK) return st;
+  if (!x || !w1 || !act || !token_scores || !block_scores) return JENGA_ERR_INVALID_ARG;
+  if (kind == JENGA_MLP_SILU_GATED && (!w_up || !aligned16(w_up))) return JENGA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(act)) return JENGA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < mlp_ws_bytes(p) || ((uintptr_t)workspace % kAlign) != 0)
+    return JENGA_ERR_WORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  jenga::ProjParams pp{};
+  pp.a = x;
+  pp.as0 = p->in_stride[0];
+  pp.as1 = p->in_stride[1];
+  pp.w = w1;
+  pp.w2 = w_up;
+  pp.out = act;
+  pp.os0 = p->out_stride[0];
+  pp.os1 = p->out_stride[1];
+  pp.B = p->batch;
+  pp.S = p->seq_len;
+  pp.K = p->in_features;
+  pp.N = p->out_features;
+  pp.block = p->block;
+  pp.nkb = p->seq_len / p->block;
+  pp.rows = p->seq_len;
+  pp.part = (float*)workspace;
+  const int mode = kind == JENGA_MLP_SILU_GATED ? jenga::kMlpGated : jenga::kMlpRelu;
+  if (jenga::launch_proj(pp, mode, kind == JENGA_MLP_SILU_GATED ? "k_mlp_act_gated" : "k_mlp_act_relu",
+                         s) != hipSuccess)
+    return JENGA_ERR_LAUNCH;
+  jenga::MlpBlockParams bp;
+  bp.part = pp.part;
+  bp.B = p->batch;
+  bp.S = p->seq_len;
+  bp.ncg = p->out_features / 32;
+  bp.F = p->out_features;
+  bp.block = p->block;
+  bp.nkb = pp.nkb;
+  bp.token_scores = token_scores;
+  bp.block_scores = block_scores;
+  return jenga::launch_mlp_block(bp, s) == hipSuccess ? JENGA_OK : JENGA_ERR_LAUNCH;
 }
 
 size_t jenga_loss_workspace_bytes(const jenga_loss_problem* p) {

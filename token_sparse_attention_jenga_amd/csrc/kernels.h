@@ -27,7 +27,7 @@ struct Eq2Params {
   float* scores;      // [B][nkb]
 };
 
-enum ProjMode { kGather = 0, kScatter = 1, kPlain = 2 };
+enum ProjMode { kGather = 0, kScatter = 1, kPlain = 2, kGatherScatter = 3, kMlpGated = 4, kMlpRelu = 5 };
 
 struct ProjParams {
   const void* a;        // bf16 input rows: gathered x [B][S][K] or compact y [B][Ncap][K]
@@ -38,7 +38,16 @@ struct ProjParams {
   const int32_t* kept;
   const int32_t* n_kept;
   int B, S, K, N, block, nkb, max_kept_blocks, ncap;
-  int rows;             // plain mode: rows of a (a multiple of 32)
+  int rows;             // plain and MLP modes: rows of a per batch row (a multiple of 32)
+  const void* w2;       // MLP gated mode: the up projection [N][K] (w is the gate projection)
+  float* part;          // MLP modes: [B][N/32][rows] sums of |activation| per 32 units
+};
+
+struct MlpBlockParams {
+  const float* part;    // [B][ncg][S]
+  int B, S, ncg, F, block, nkb;
+  float* token_scores;  // [B][S]
+  float* block_scores;  // [B][nkb]
 };
 
 struct CeParams {
@@ -108,6 +117,8 @@ hipError_t launch_score64(const ScoreParams& p, int D, hipStream_t st);
 
 // projections (proj.hip): gathered input rows, scatter-add into resid, or plain rows
 hipError_t launch_proj(const ProjParams& p, int mode, const char* name, hipStream_t st);
+
+hipError_t launch_mlp_block(const MlpBlockParams& p, hipStream_t st);
 
 // language-model-head loss (loss.hip)
 hipError_t launch_ce_rows(const CeParams& p, hipStream_t st);
