@@ -456,6 +456,14 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
       sacc = Mfma<bf16>::mma(ldo(Ql, rp.nat[s]), ldo(Kw, rp.nat[s]), sacc);
       pacc = Mfma<bf16>::mma(ldo(dOl, rp.nat[s]), vf[s], pacc);
     }
+    // operand reads run one k-step ahead of the MFMAs that consume them
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int s = 0; s < C::NS - 2; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // lane = key kw0 + lc; register r = query q0 + 8(r/4) + 4hl + r%4
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
@@ -470,10 +478,11 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
       }
     }
     if (q0 < kw0 + 31) {                                          // diagonal step: causal mask
-      const int kr = kw0 + lc;
+      // query q0 + 8(r/4) + 4hl + r%4 < key kw0 + lc  <=>  8(r/4) + r%4 < kw0 + lc - q0 - 4hl
+      const int lim = kw0 + lc - q0 - 4 * hl;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (q0 + 8 * (r >> 2) + 4 * hl + (r & 3) < kr) {
+        if (8 * (r >> 2) + (r & 3) < lim) {
           sacc[r] = 0.f;
           pacc[r] = 0.f;
         }
@@ -487,6 +496,14 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
         dk[db] = Mfma<bf16>::mma(sf, ldo(QTl + db * 2048, rp.tp[j]), dk[db]);
       }
     }
+    // operand reads run two MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 2 * C::NDB * 2 / 2 - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   };
 
   if (nsteps > 0) {
