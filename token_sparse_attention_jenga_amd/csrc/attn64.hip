@@ -172,13 +172,15 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
 #pragma unroll
       for (int qb = 0; qb < NB; ++qb) st[qb] = Mfma<bf16>::mma(a, qf[qb][s], st[qb]);
     }
+    SCHED_READS_AHEAD(C::NS, 1, NB, 0);
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
       if (kr0 + 31 > qw0 + 32 * qb) {                      // diagonal step: causal mask
-        const int qr = qw0 + 32 * qb + lc;
+        // key kr0 + 8(r/4) + 4hl + r%4 > query qw0 + 32qb + lc  <=>  8(r/4) + r%4 > lim
+        const int lim = qw0 + 32 * qb + lc - kr0 - 4 * hl;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) > qr) st[qb][r] = -INFINITY;
+          if (8 * (r >> 2) + (r & 3) > lim) st[qb][r] = -INFINITY;
       }
       float mx = st[qb][0];
 #pragma unroll
@@ -216,6 +218,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
         for (int qb = 0; qb < NB; ++qb) o[qb][db] = Mfma<bf16>::mma(va, pf[qb], o[qb][db]);
       }
     }
+    SCHED_READS_AHEAD(2 * C::NDB, 1, NB, 1);
   };
 
   // three-buffer ring: the tiles of step t+2 load while step t computes
@@ -456,14 +459,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
       sacc = Mfma<bf16>::mma(ldo(Ql, rp.nat[s]), ldo(Kw, rp.nat[s]), sacc);
       pacc = Mfma<bf16>::mma(ldo(dOl, rp.nat[s]), vf[s], pacc);
     }
-    // operand reads run one k-step ahead of the MFMAs that consume them
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int s = 0; s < C::NS - 2; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    SCHED_READS_AHEAD(C::NS, 3, 2, 0);
     // lane = key kw0 + lc; register r = query q0 + 8(r/4) + 4hl + r%4
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
@@ -496,14 +492,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
         dk[db] = Mfma<bf16>::mma(sf, ldo(QTl + db * 2048, rp.tp[j]), dk[db]);
       }
     }
-    // operand reads run two MFMAs ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-    for (int i = 0; i < 2 * C::NDB * 2 / 2 - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+    SCHED_READS_AHEAD(2 * C::NDB, 2, 2, 1);
   };
 
   if (nsteps > 0) {
@@ -656,6 +645,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
         dp[qb] = Mfma<bf16>::mma(av, df[qb][s], dp[qb]);
       }
     }
+    SCHED_READS_AHEAD(C::NS, 2, 2 * NB, 0);
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
 #pragma unroll
@@ -664,10 +654,10 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
         st[qb][r] = pv * (dp[qb][r] - Dv[qb]);
       }
       if (kr0 + 31 > qw0 + 32 * qb) {                            // diagonal step: causal mask
-        const int qr = qw0 + 32 * qb + lc;
+        const int lim = qw0 + 32 * qb + lc - kr0 - 4 * hl;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) > qr) st[qb][r] = 0.f;
+          if (8 * (r >> 2) + (r & 3) > lim) st[qb][r] = 0.f;
       }
     }
 #pragma unroll
@@ -682,6 +672,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
         for (int qb = 0; qb < NB; ++qb) acc[qb][db] = Mfma<bf16>::mma(af[qb], bk, acc[qb][db]);
       }
     }
+    SCHED_READS_AHEAD(2 * C::NDB, 1, NB, 1);
   };
 
   auto stage = [&](int t, const char* cur, char* nxt) {

@@ -64,6 +64,22 @@ __device__ inline void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Scheduling groups for a run of NSTEP k-steps, each READS LDS operand reads feeding MFMAS
+// MFMAs, placed right after that run in the same basic block: the reads of step i+1 are issued
+// before the MFMAs of step i, so each MFMA finds its operands already on the way instead of
+// waiting out a whole LDS round trip (left alone, the compiler pairs each read with its use).
+// Runs that can end up in one basic block take different SYNC ids.
+// (A macro, not a function: the groups then stay attached to the caller's instructions.)
+#define SCHED_READS_AHEAD(NSTEP, READS, MFMAS, SYNC)                                             \
+  do {                                                                                          \
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (READS), SYNC); /* reads of steps 0, 1 */  \
+    _Pragma("unroll") for (int i_ = 0; i_ < (NSTEP) - 2; ++i_) {                                \
+      __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, SYNC);     /* MFMAs of step i */       \
+      __builtin_amdgcn_sched_group_barrier(0x100, READS, SYNC);     /* reads of step i + 2 */   \
+    }                                                                                           \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * (MFMAS), SYNC); /* last two steps */        \
+  } while (0)
+
 // Workgroup barrier for the staged loops.  __syncthreads() also fences memory, which makes
 // the compiler wait for every outstanding vector-memory operation -- including the
 // direct-to-LDS loads of tiles still being prefetched.  Here each wave first waits for its own
