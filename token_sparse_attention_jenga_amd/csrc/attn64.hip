@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
       float mx = st[qb][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[qb][r]);
-      mx = fmaxf(mx, wave_xor32(mx)) * c2;               // row max in the log2 domain
+      mx = half_pair_max(mx) * c2;               // row max in the log2 domain
       // lazy rescale: move the reference max only when it grows by kLazyRescale or more
       const bool grow = mx > m_run[qb] + kLazyRescale;
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
 #pragma unroll
   for (int qb = 0; qb < NB; ++qb) {
     const int qr = qw0 + 32 * qb + lc;
-    const float lsum = l_run[qb] + wave_xor32(l_run[qb]);
+    const float lsum = half_pair_sum(l_run[qb]);
     const float inv = 1.f / lsum;
     float* rrow = p.resid + (((int64_t)b * p.S + qpos[qb]) * p.Hq + h) * D;
     char* orow = (char*)p.o_saved + ((((int64_t)b * p.ncap + qr) * p.Hq + h) * D) * 2;

@@ -109,6 +109,18 @@ __device__ inline void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 
 __device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Combine lane l with lane l ^ 32 through the cross-half lane swap (a VALU operation, no LDS
+// round trip): the swap of x with itself returns (x[l], x[l + 32]) in lanes l < 32 and
+// (x[l - 32], x[l]) in lanes l >= 32, so both lanes of a pair see the same two values.
+__device__ inline float half_pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float half_pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // XCD-aware workgroup numbering.  An MI355X has 8 XCDs, each with its own L2, and the
 // dispatcher hands workgroups, in linear launch order, to XCD (index % 8) in turn.  xcd_tile()
 // renumbers them so that XCD x runs one contiguous range of logical tiles (x fastest, then y,

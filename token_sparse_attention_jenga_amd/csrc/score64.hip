@@ -75,7 +75,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
     float mx = st[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
-    mx = fmaxf(mx, wave_xor32(mx)) * c2;
+    mx = half_pair_max(mx) * c2;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kScoreLazy) != 0) {
       const float m_new = fmaxf(m_run, mx);
       l_run *= (double)__builtin_amdgcn_exp2f(m_run - m_new);
