@@ -233,13 +233,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
   };
   issue(0, sA);
   issue(min(1, nsteps - 1), sB);
-  for (int t = 0; t < nsteps; t += 3) {
-    stage(t, sA, sC);
-    if (t + 1 >= nsteps) break;
-    stage(t + 1, sB, sA);
-    if (t + 2 >= nsteps) break;
-    stage(t + 2, sC, sB);
-  }
+  ring3_loop(nsteps, sA, sB, sC, stage);
   wait_all_mem();                                        // drain the trailing reloads
 
   if (!active) return;
@@ -686,13 +680,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
   };
   issue(0, sA);
   issue(min(1, nsteps - 1), sB);
-  for (int t = 0; t < nsteps; t += 3) {
-    stage(t, sA, sC);
-    if (t + 1 >= nsteps) break;
-    stage(t + 1, sB, sA);
-    if (t + 2 >= nsteps) break;
-    stage(t + 2, sC, sB);
-  }
+  ring3_loop(nsteps, sA, sB, sC, stage);
   wait_all_mem();                                        // drain the trailing reloads
 
   if (!active) return;

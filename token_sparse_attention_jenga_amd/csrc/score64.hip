@@ -59,7 +59,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
   float m_run = -INFINITY;
   double l_run = 0.0;
 
-  const rsrc_t rk = make_rsrc(kbase);
+  const rsrc_t rk = make_rsrc_u(kbase);
   auto issue = [&](int t, char* buf) { kplan.issue(buf, rk, (uint32_t)(32 * t * kstride)); };
   auto compute = [&](int t, const char* Kl) {
     const int kr0 = 32 * t;
@@ -97,13 +97,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
   };
   issue(0, sA);
   issue(min(1, nsteps - 1), sB);
-  for (int t = 0; t < nsteps; t += 3) {
-    stage(t, sA, sC);
-    if (t + 1 >= nsteps) break;
-    stage(t + 1, sB, sA);
-    if (t + 2 >= nsteps) break;
-    stage(t + 2, sC, sB);
-  }
+  ring3_loop(nsteps, sA, sB, sC, stage);
   wait_all_mem();                                        // drain the trailing reloads
   if (!active) return;
   const double lsum = l_run + __shfl_xor(l_run, 32, 64);
@@ -153,7 +147,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_smass64(ScoreParams p) {
   const float c2 = p.scale_log2;
   double acc = 0.0;
 
-  const rsrc_t rq = make_rsrc(qbase), rl = make_rsrc(lrow);
+  const rsrc_t rq = make_rsrc_u(qbase), rl = make_rsrc_u(lrow);
   const uint32_t lvoff = 16u * (LDC * w + l);
   auto issue = [&](int t, char* buf) {
     const int q0 = k0 + 32 * t;
@@ -200,13 +194,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_smass64(ScoreParams p) {
   if (nsteps > 0) {
     issue(0, sA);
     issue(min(1, nsteps - 1), sB);
-    for (int t = 0; t < nsteps; t += 3) {
-      stage(t, sA, sC);
-      if (t + 1 >= nsteps) break;
-      stage(t + 1, sB, sA);
-      if (t + 2 >= nsteps) break;
-      stage(t + 2, sC, sB);
-    }
+    ring3_loop(nsteps, sA, sB, sC, stage);
   }
   wait_all_mem();                                        // drain the trailing reloads
   // lanes l and l^32 hold the same key; then a fixed butterfly over the wave's 32 keys

@@ -49,6 +49,17 @@ __device__ inline rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
 }
 
+// The same for a base that is the same in every lane of the wave, taken through readfirstlane
+// so that the resource is built in scalar registers: where the compiler cannot prove the
+// address uniform it otherwise keeps the resource in vector registers and wraps every load
+// that uses it in a waterfall loop.
+__device__ inline rsrc_t make_rsrc_u(const void* base) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return make_rsrc((const void*)(uintptr_t)(lo | (hi << 32)));
+}
+
 __device__ inline void dma16b(rsrc_t r, uint32_t voff, uint32_t soff, char* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, voff, soff, 0, 0);
 }
@@ -79,6 +90,28 @@ __device__ inline void wait_vm() {
     }                                                                                           \
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * (MFMAS), SYNC); /* last two steps */        \
   } while (0)
+
+// The staged loop over a three-buffer LDS ring: stage(t, cur, nxt) computes tile t from cur
+// while tile t + 2 loads into nxt (tile t lives in buffer t % 3).  Six steps per iteration:
+// where the loop's back edge joins, the compiler no longer knows which buffer a pending
+// direct-to-LDS load targets and makes the first buffer read after the join wait for all of
+// them; with six steps per iteration that exposed wait comes once per six steps, not three.
+template <class Stage>
+__device__ inline void ring3_loop(int n, char* A, char* B, char* C, Stage&& stage) {
+  for (int t = 0; t < n; t += 6) {
+    stage(t, A, C);
+    if (t + 1 >= n) break;
+    stage(t + 1, B, A);
+    if (t + 2 >= n) break;
+    stage(t + 2, C, B);
+    if (t + 3 >= n) break;
+    stage(t + 3, A, C);
+    if (t + 4 >= n) break;
+    stage(t + 4, B, A);
+    if (t + 5 >= n) break;
+    stage(t + 5, C, B);
+  }
+}
 
 // Workgroup barrier for the staged loops.  __syncthreads() also fences memory, which makes
 // the compiler wait for every outstanding vector-memory operation -- including the
@@ -158,7 +191,9 @@ struct NatPlan {
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < MAXW; ++i)
-      if (w + i * NW < NI) dma16b(r, off[i], soff, lds_tile + (w + i * NW) * 1024);
+      // (when NW divides the load count every wave issues all of its loads; the bound check
+      // then stays out of the code, so the loads are not placed in branches of their own)
+      if (NI % NW == 0 || w + i * NW < NI) dma16b(r, off[i], soff, lds_tile + (w + i * NW) * 1024);
   }
 };
 
@@ -181,7 +216,7 @@ struct TpPlan {
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < MAXW; ++i)
-      if (w + i * NW < NI) dma16b(r, off[i], soff, lds_tile + (w + i * NW) * 1024);
+      if (NI % NW == 0 || w + i * NW < NI) dma16b(r, off[i], soff, lds_tile + (w + i * NW) * 1024);
   }
 };
 
