@@ -54,18 +54,32 @@ def parse():
     return ap.parse_args()
 
 
+# The sources the dominant kernel (k_dkdv32) is compiled from: its traffic counters stay valid
+# while these are unchanged.
+ROOFLINE_SOURCES = ("attn64.hip", "tiles64.h", "common.h", "kernels.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "token_sparse_attention_jenga_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in ROOFLINE_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
+# k_proj<MODE> instances (one template, several launch names: the logits and dL/dh products of
+# the loss are both the plain mode)
+PROJ_MODES = {0: "k_proj<gather>", 1: "k_proj<scatter>", 2: "k_proj<plain>",
+              3: "k_proj<gather_scatter>", 4: "k_proj<mlp_gated>", 5: "k_proj<mlp_relu>"}
+
+
 def _short(name: str) -> str:
-    for k in KERNELS + ("k_score_reduce",):
+    for mode, label in PROJ_MODES.items():
+        if f"::k_proj<{mode}>" in name:
+            return label
+    for k in KERNELS + ("k_score_reduce", "k_loss_mean"):
         if f"::{k}<" in name or f"::{k}(" in name:
             return k
     if "neg_kernel" in name:
