@@ -11,8 +11,9 @@
 //   k_eq2_tiles   one workgroup per causal score block: loops over the query heads, S^h = Q K^T
 //                 per 32x32 sub-tile with MFMA, acc += max(S^h, 0); then the causal mask on the
 //                 diagonal block and the block maximum, times c / Hq (c > 0 factors out of the
-//                 positive part and the maximum).  Q and K tiles of the next head load into a
-//                 second LDS buffer while the current head is processed.
+//                 positive part and the maximum).  Q and K tiles load in 64-column chunks of
+//                 head_dim; the next chunk loads into a second LDS buffer while the current one
+//                 is multiplied.
 //   k_eq2_reduce  s_n = sum over m >= n in a fixed order (fp64), rounded once to fp32.
 #include "common.h"
 #include "kernels.h"
@@ -20,23 +21,55 @@
 
 namespace jenga {
 
-// Causal score block (m, n), m >= n, of linear index t in m-major order: t = m(m+1)/2 + n.
-__device__ inline void pair_of(int t, int& m, int& n) {
-  int mm = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
-  while ((mm + 1) * (mm + 2) / 2 <= t) ++mm;
-  while (mm * (mm + 1) / 2 > t) --mm;
-  m = mm;
-  n = t - mm * (mm + 1) / 2;
+// Score blocks are visited in super-tiles of kSM query blocks x kSN key blocks, one
+// workgroup per block: the kSM * kSN = 32 workgroups an XCD runs at a time (one per compute
+// unit) then share kSM Q and kSN K blocks per head in that XCD's L2, instead of one Q block
+// and 32 different K blocks.  Super-tile (M, N) holds the blocks m in [kSM M, kSM M + kSM),
+// n in [kSN N, kSN N + kSN); only super-tiles holding some causal block (m >= n) are
+// launched, N-major, and slots with m < n or past the last block exit at once.
+constexpr int kSM = 4, kSN = 8;
+
+__host__ __device__ inline int eq2_super_rows(int nkb) { return (nkb + kSM - 1) / kSM; }
+// first super-row M holding a causal block of super-column N: kSM M + kSM - 1 >= kSN N
+__host__ __device__ inline int eq2_first_row(int N) {
+  const int need = kSN * N - (kSM - 1);
+  return need <= 0 ? 0 : (need + kSM - 1) / kSM;
+}
+__host__ __device__ inline int eq2_super_tiles(int nkb) {
+  const int R = eq2_super_rows(nkb), Cn = (nkb + kSN - 1) / kSN;
+  int n = 0;
+  for (int N = 0; N < Cn; ++N) n += R - eq2_first_row(N);
+  return n;
+}
+
+// (m, n) of workgroup slot t; false for a slot without a causal block
+__device__ inline bool pair_of(int t, int nkb, int& m, int& n) {
+  const int slot = t % (kSM * kSN);
+  int st = t / (kSM * kSN), N = 0;
+  const int R = eq2_super_rows(nkb);
+  for (;;) {
+    const int cnt = R - eq2_first_row(N);
+    if (st < cnt) break;
+    st -= cnt;
+    ++N;
+  }
+  m = kSM * (eq2_first_row(N) + st) + slot / kSN;
+  n = kSN * N + slot % kSN;
+  return m < nkb && n <= m;
 }
 
 template <int D, int BLK>
-__global__ __launch_bounds__(256, 1) void k_eq2_tiles(Eq2Params p) {
-  using C = T64<D>;
+__global__ __launch_bounds__(256, 2) void k_eq2_tiles(Eq2Params p) {
+  // Tiles are staged in 64-column chunks of head_dim (the scores of a head are summed over its
+  // chunks before the positive part is taken): a stage is then small enough for two
+  // workgroups per compute unit, each covering the other's load latency.
+  using C = T64<64>;
+  constexpr int DC = D / 64;                              // head_dim chunks per head
   constexpr int NW = 4;
   constexpr int SB = BLK / 32;                            // 32-row sub-blocks per block
   constexpr int SPW = SB * SB / NW;                       // sub-tiles per wave
   static_assert(SPW >= 1 && SB * SB == SPW * NW, "block must be 64 or 128");
-  constexpr int STAGE = 2 * SB * C::NAT32;                // Q tiles then K tiles of one head
+  constexpr int STAGE = 2 * SB * C::NAT32;                // Q tiles then K tiles of one chunk
   __shared__ __attribute__((aligned(1024))) char sA[STAGE];
   __shared__ __attribute__((aligned(1024))) char sB[STAGE];
   __shared__ float wmax[NW];
@@ -44,58 +77,66 @@ __global__ __launch_bounds__(256, 1) void k_eq2_tiles(Eq2Params p) {
   const Tile3 tl = xcd_tile();
   const int b = tl.y;
   int m, n;
-  pair_of(tl.x, m, n);
+  if (!pair_of(tl.x, p.nkb, m, n)) return;
   const int G = p.Hq / p.Hkv;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
 
   const int64_t qstride = p.qs[1] * 2, kstride = p.ks[1] * 2;
-  NatPlan<D, NW> qplan, kplan;
+  NatPlan<64, NW> qplan, kplan;
   qplan.init(qstride);
   kplan.init(kstride);
-  ReadPlan<D> rp;
+  ReadPlan<64> rp;
   rp.init();
   const rsrc_t rq = make_rsrc((const bf16*)p.q + b * p.qs[0]);
   const rsrc_t rk = make_rsrc((const bf16*)p.k + b * p.ks[0]);
-  auto issue = [&](int h, char* buf) {
-    const int g = h / G;
+  const int nu = p.Hq * DC;                               // (head, chunk) steps
+  auto issue = [&](int u, char* buf) {
+    const int h = u / DC, c = u - h * DC, g = h / G;
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
-      qplan.issue(buf + sb * C::NAT32, rq, (uint32_t)((h * p.qs[2] + (int64_t)(m * BLK + 32 * sb) * p.qs[1]) * 2));
-      kplan.issue(buf + (SB + sb) * C::NAT32, rk, (uint32_t)((g * p.ks[2] + (int64_t)(n * BLK + 32 * sb) * p.ks[1]) * 2));
+      qplan.issue(buf + sb * C::NAT32, rq,
+                  (uint32_t)((h * p.qs[2] + (int64_t)(m * BLK + 32 * sb) * p.qs[1]) * 2 + 128 * c));
+      kplan.issue(buf + (SB + sb) * C::NAT32, rk,
+                  (uint32_t)((g * p.ks[2] + (int64_t)(n * BLK + 32 * sb) * p.ks[1]) * 2 + 128 * c));
     }
   };
 
-  f32x16 acc[SPW];
+  f32x16 acc[SPW], sc[SPW];
 #pragma unroll
-  for (int t = 0; t < SPW; ++t) acc[t] = zero16();
+  for (int t = 0; t < SPW; ++t) acc[t] = sc[t] = zero16();
   // sub-tile t of this wave: query sub-block qsb(t), key sub-block ksb(t)
   auto qsb = [&](int t) { return (w * SPW + t) / SB; };
   auto ksb = [&](int t) { return (w * SPW + t) % SB; };
 
-  auto compute = [&](const char* buf) {
+  auto compute = [&](int u, const char* buf) {
 #pragma unroll
     for (int t = 0; t < SPW; ++t) {
       const char* Qt = buf + qsb(t) * C::NAT32;
       const char* Kt = buf + (SB + ksb(t)) * C::NAT32;
-      f32x16 st = zero16();
 #pragma unroll
-      for (int s = 0; s < C::NS; ++s) st = Mfma<bf16>::mma(ldo(Qt, rp.nat[s]), ldo(Kt, rp.nat[s]), st);
+      for (int s = 0; s < C::NS; ++s) sc[t] = Mfma<bf16>::mma(ldo(Qt, rp.nat[s]), ldo(Kt, rp.nat[s]), sc[t]);
+    }
+    if (u % DC == DC - 1) {                               // a head's scores are complete
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] += fmaxf(st[r], 0.f);
+      for (int t = 0; t < SPW; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] += fmaxf(sc[t][r], 0.f);
+        sc[t] = zero16();
+      }
     }
   };
 
   issue(0, sA);
   wait_all_mem();
   __syncthreads();
-  for (int h = 0; h < p.Hq; h += 2) {
-    if (h + 1 < p.Hq) issue(h + 1, sB);
-    compute(sA);
+  for (int u = 0; u < nu; u += 2) {
+    if (u + 1 < nu) issue(u + 1, sB);
+    compute(u, sA);
     wait_all_mem();
     stage_barrier();
-    if (h + 1 >= p.Hq) break;
-    if (h + 2 < p.Hq) issue(h + 2, sA);
-    compute(sB);
+    if (u + 1 >= nu) break;
+    if (u + 2 < nu) issue(u + 2, sA);
+    compute(u + 1, sB);
     wait_all_mem();
     stage_barrier();
   }
@@ -134,7 +175,7 @@ __global__ __launch_bounds__(256) void k_eq2_reduce(Eq2Params p) {
 
 template <int D, int BLK>
 static hipError_t launch_eq2_t(const Eq2Params& p, hipStream_t st) {
-  const int pairs = p.nkb * (p.nkb + 1) / 2;
+  const int pairs = eq2_super_tiles(p.nkb) * kSM * kSN;         // workgroup slots
   {
     TimedLaunch tl("k_eq2_tiles", st);
     k_eq2_tiles<D, BLK><<<dim3(pairs, p.B), 256, 0, st>>>(p);
