@@ -75,6 +75,10 @@ __global__ __launch_bounds__(512, 1) void k_proj(ProjParams p) {
   const KeptTab kt{(const LDS_AS int*)ktab, kept, p.block};
   const int tid = threadIdx.x, l = tid & 63, hl = l >> 5, lc = l & 31;
   const int w = tid >> 6;
+  // the same wave index taken through readfirstlane, for what the direct-to-LDS loads need in
+  // scalar registers (row offsets, LDS destination): computed from the plain index the
+  // compiler cannot prove them uniform and wraps every load in a waterfall loop
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w & 3, wn = w >> 2;                       // the wave's 64-row / 64-column group
 
   // Load j = w + 8i of a chunk (i = 0..5) covers quarter (w % 4) of tile 2i + w/4: tiles 0..7
@@ -85,15 +89,12 @@ __global__ __launch_bounds__(512, 1) void k_proj(ProjParams p) {
   const int64_t abytes = p.as1 * 2, wbytes = (int64_t)p.K * 2;
   const uint32_t voff_a = (uint32_t)(trow * abytes + tchunk);
   const uint32_t voff_w = (uint32_t)(trow * wbytes + tchunk);
-  const int tsel = w >> 2;
-  const rsrc_t ra = make_rsrc((const bf16*)p.a + b * p.as0);
+  const int tsel = wu >> 2;
+  const rsrc_t ra = make_rsrc_u((const bf16*)p.a + b * p.as0);
   // Gated mode: W tile slot 2i + tsel holds rows c0 + 32i of the gate (tsel 0) or the up
   // projection (tsel 1), c0 = 64 nt, so wave column group wn reads gate and up of units
   // c0 + 32wn .. +31.  Otherwise slot t holds W rows n0 + 32t.
-  // (tsel is the same in every lane of a wave; readfirstlane keeps the choice in scalar registers.
-  // The wave index itself is left as computed: a readfirstlane there hides the LDS addresses
-  // of the loads from the compiler, which then drains every load before each chunk.)
-  const rsrc_t rw = make_rsrc(GATED && __builtin_amdgcn_readfirstlane(tsel) ? p.w2 : p.w);
+  const rsrc_t rw = make_rsrc_u(GATED && tsel ? p.w2 : p.w);
   auto wrow = [&](int i) -> int64_t { return GATED ? nt * 64 + 32 * i : n0 + 32 * (2 * i + tsel); };
   // first row of A tile t (rows past the row count load a harmless valid row instead, so
   // that every wave issues the same number of loads per chunk)
@@ -110,11 +111,11 @@ __global__ __launch_bounds__(512, 1) void k_proj(ProjParams p) {
     const uint32_t koff = (uint32_t)c * 128u;               // 64 bf16 per chunk
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      dma16b(ra, voff_a, (uint32_t)abase[i] + koff, buf + (2 * i + tsel) * C::NAT32 + (w & 3) * 1024);
+      dma16b(ra, voff_a, (uint32_t)abase[i] + koff, buf + (2 * i + tsel) * C::NAT32 + (wu & 3) * 1024);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       dma16b(rw, voff_w, (uint32_t)(wrow(i) * wbytes) + koff,
-             buf + (AT + 2 * i + tsel) * C::NAT32 + (w & 3) * 1024);
+             buf + (AT + 2 * i + tsel) * C::NAT32 + (wu & 3) * 1024);
   };
 
   ReadPlan<64> rp;
