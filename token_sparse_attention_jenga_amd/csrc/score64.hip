@@ -67,6 +67,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
     f32x16 st = zero16();
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) st = Mfma<bf16>::mma(ldo(Kl, rp.nat[s]), qf[s], st);
+    SCHED_READS_AHEAD(C::NS, 1, 1, 0);
     if (kr0 + 31 > qw0) {                                // diagonal step: causal mask
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -160,6 +161,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_smass64(ScoreParams p) {
     f32x16 st = zero16();
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) st = Mfma<bf16>::mma(ldo(buf, rp.nat[s]), kf[s], st);
+    SCHED_READS_AHEAD(C::NS, 1, 1, 0);
     const float* ls = (const float*)(buf + C::NAT32);
     float colsum = 0.f;
     if (q0 <= kw0 + 31) {                          // diagonal step: only queries after the key
