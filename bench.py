@@ -311,7 +311,7 @@ def main():
         avg_ms = t_dkdv / n_dkdv
         achieved = dkdv_flop_launch / (avg_ms * 1e-3) / 1e12
         traffic = None
-        tfile = os.path.join(ROOT, "profiles", f"traffic_k_dkdv32_{cfg.name}.json")
+        tfile = os.path.join(ROOT, "profiles", f"traffic_k_dkdv32_{args.config}.json")
         if os.path.exists(tfile) and args.kept == "selected" and nseg == cfg.n_segments:
             with open(tfile) as f:
                 tj = json.load(f)
