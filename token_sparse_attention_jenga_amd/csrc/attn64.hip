@@ -536,7 +536,8 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
 }
 
 // ------------------------------------------------------------------------------------------
-// dQ: query-major.  Workgroup = 2 waves x 64 kept queries of one query head.
+// dQ: query-major.  Workgroup = NW waves x 32 kept queries of one query head (NW = 8: the K, V
+// and K-transposed tiles of a step serve 256 queries; two waves per SIMD either way).
 // ------------------------------------------------------------------------------------------
 template <int D, int NB, int NW>
 __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) {
@@ -710,7 +711,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
 // Shapes: *_NB 32-row blocks per wave, *_NW waves per workgroup.
 constexpr int FWD_NB = 1, FWD_NW = 4;
 constexpr int DKDV_NW = 8;
-constexpr int DQ_NB = 1, DQ_NW = 4;
+constexpr int DQ_NB = 1, DQ_NW = 8;
 
 template <int D>
 static hipError_t launch_fwd64_t(const FwdParams& p, hipStream_t st) {
