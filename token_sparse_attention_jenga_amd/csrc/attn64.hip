@@ -413,6 +413,10 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
   constexpr int LDC = 16 / NW;
   static_assert(16 % NW == 0, "lse/D chunks must split evenly over the waves");
   const int ld_chunk = LDC * w + l;
+  // LDS offset of this wave's lse2/D chunks, from the wave index taken through readfirstlane:
+  // derived from the plain index it sits in a vector register, which the compiler spilled and
+  // reloaded in the loop -- a scratch load whose wait drained the tile loads just issued
+  const int ld_lds = 16 * LDC * __builtin_amdgcn_readfirstlane(w);
 
   const rsrc_t rq = make_rsrc((const bf16*)p.q + b * p.qs[0]);
   const rsrc_t rdo = make_rsrc((const char*)p.wsdO + (int64_t)b * p.seg_len * p.Hq * D * 2);
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
     tplan.issue(buf + OFF_QT, rqt, tile);
     tplan.issue(buf + OFF_DOT, rdot, tile);
     if (l < LDC)
-      dma16b(rld, ld_voff, (uint32_t)((h * p.seg_len + (q0 - qs)) * 4), buf + OFF_LD + 16 * LDC * w);
+      dma16b(rld, ld_voff, (uint32_t)((h * p.seg_len + (q0 - qs)) * 4), buf + OFF_LD + ld_lds);
   };
 
   auto compute = [&](int step, const char* buf) {
