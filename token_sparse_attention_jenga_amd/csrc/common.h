@@ -105,7 +105,6 @@ __device__ inline int rank_to_pos(const int32_t* __restrict__ kept, int block, i
 
 // 16-byte global load / store helpers.
 __device__ inline u32x4 ld16(const void* p) { return *(const u32x4*)p; }
-__device__ inline void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 
 __device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -32,10 +32,6 @@ struct T64 {
   static constexpr int NDB = D / 32;       // 32-wide head_dim blocks
 };
 
-__device__ inline void dma16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)lds, 16, 0, 0);
-}
-
 // Direct-to-LDS copies through raw buffer loads.  The resource holds a wave-uniform base (kept in
 // SGPRs); a copy adds a per-lane offset (voff, a register computed once per kernel) and a
 // wave-uniform one (soff, per step).  Keeping the per-lane part in a long-lived register matters:
@@ -135,36 +131,7 @@ struct DmaCount {
   static constexpr int NAT_W = NAT / NW, TP_W = TP / NW;
 };
 
-// Natural 32-row tile: rows at g_row0 + r * row_stride (bytes).  NW waves share the copy.
-template <int D, int NW>
-__device__ inline void dma_nat32(char* lds_tile, const char* g_row0, int64_t row_stride) {
-  constexpr int CPR = T64<D>::CPR;
-  constexpr int NI = 32 * CPR / 64;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-#pragma unroll
-  for (int n = w; n < NI; n += NW) {
-    const int idx = n * 64 + l;
-    const int row = idx / CPR, phys = idx % CPR;
-    const int c = phys ^ (row & (CPR - 1));
-    dma16(g_row0 + row * row_stride + c * 16, lds_tile + n * 1024);
-  }
-}
-
 __device__ inline int tpswz(int d) { return ((d >> 1) & 3) ^ ((d >> 3) & 1); }
-
-// TP tile: a contiguous [D][32] bf16 block in global memory.
-template <int D, int NW>
-__device__ inline void dma_tp32(char* lds_tile, const char* g_tile) {
-  constexpr int NI = D * 64 / 1024;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-#pragma unroll
-  for (int n = w; n < NI; n += NW) {
-    const int idx = n * 64 + l;
-    const int d = idx >> 2, phys = idx & 3;
-    const int c = phys ^ tpswz(d);
-    dma16(g_tile + d * 64 + c * 16, lds_tile + n * 1024);
-  }
-}
 
 // Per-lane address offsets of one wave's direct-to-LDS instructions, computed once per kernel
 // so that a step only adds its (wave-uniform) base address.  The offsets are unsigned 32-bit so
@@ -238,15 +205,6 @@ struct ReadPlan {
 };
 
 __device__ inline bf16x8 ldo(const char* tile, int off) { return *(const bf16x8*)(tile + off); }
-
-template <int D>
-__device__ inline bf16x8 ld_nat(const char* tile, int row, int c) {
-  return *(const bf16x8*)(tile + row * T64<D>::ROWB + ((c ^ (row & (T64<D>::CPR - 1))) << 4));
-}
-
-__device__ inline bf16x8 ld_tp(const char* tile, int d, int c) {
-  return *(const bf16x8*)(tile + d * 64 + ((c ^ tpswz(d)) << 4));
-}
 
 // Kept-block table staged in LDS once per workgroup, so the hot loops resolve a kept rank to
 // its token position without a global-memory round trip.  Blocks beyond the table's capacity
