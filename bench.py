@@ -478,6 +478,67 @@ def main():
            "fwd_workspace_mib": round(layers[0]["ws_f"].numel() / 2**20, 2),
            "bwd_workspace_mib": round(layers[0]["ws_b"].numel() / 2**20, 2)}
 
+    # Per-step evidence beside the metric: the exponentials per second of the two scoring passes
+    # (one exp per causal pair per query head in each pass), and the backward prologue's
+    # bytes per second (per kept query row and head: dOut row fp32 and o_saved row in, lse in;
+    # D, lse2, the dOut row in operand dtype and its transposed copy out).
+    es = 2 if cfg.dtype == "bf16" else 4
+    score_exps = 2.0 * Hq * B * L * S * (S + 1) / 2
+    step_evidence = {"score_exp_per_s": round(score_exps / (phase["score"] * 1e-3), 1)}
+    n_prep, t_prep = kern_ms.get("k_prep64", (0, 0.0))
+    if n_prep:
+        prep_bytes = float(sum(sum(per) for per in nks)) * Hq * (4 * D + 2 * es * D + es * D + 12) / n_prep * K
+        step_evidence["prep_gbs"] = round(prep_bytes / (t_prep / n_prep * 1e-3) / 1e9, 1)
+
+    # The same fwd+bwd over the layers with a seeded scattered kept set per layer (the selected
+    # sets of this workload come out nearly contiguous): same kept count, so the same FLOPs.
+    scattered = None
+    if args.kept == "selected" and cfg.select_mode == "topk":
+        for l, st in enumerate(layers):
+            kb = random_kept_blocks(nkb, maxk, 5999 + l)
+            arr = np.full((B, nkb), -1, np.int32)
+            arr[:, :maxk] = kb
+            st["kept_sc"] = torch.from_numpy(arr).to(dev)
+            st["nk_sc"] = torch.full((B,), maxk, dtype=torch.int32, device=dev)
+
+        def attn_pass():
+            for st in layers:
+                J.jenga_sparse_attn_fwd(st["p"], st["q"], st["k"], st["v"], st["kept_sc"], st["nk_sc"], maxk,
+                                        resid, st["o"], st["lse"], st["ws_f"])
+            for l in reversed(range(L)):
+                st = layers[l]
+                J.jenga_sparse_attn_bwd_segmented(st["p"], st["q"], st["k"], st["v"], st["kept_sc"],
+                                                  st["nk_sc"], maxk, st["o"], st["lse"], dout, st["dq"],
+                                                  st["dk"], st["dv"], nseg, st["ws_b"])
+        attn_pass()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, min(K, 3))
+        s0.record(stream)
+        for _ in range(reps):
+            attn_pass()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        sc_ms = s0.elapsed_time(s1) / reps
+        sc_pairs = L * B * (maxk * blk) * (maxk * blk + 1) / 2
+        scattered = {"kept": f"default_rng(5999 + layer) choice of {maxk} of {nkb} blocks, sorted",
+                     "attn_ms_per_step": round(sc_ms, 3),
+                     "tflops": round(14.0 * D * Hq * sc_pairs / (sc_ms * 1e-3) / 1e12, 2)}
+
+    # Memory at this workload's shapes, one layer, over keep ratios and segment counts: the
+    # activations the backward keeps (o_saved, lse, the kept list) and the backward's transient,
+    # which is exactly its workspace (the library allocates nothing else).
+    memory_sweep = []
+    if cfg.dtype == "bf16":
+        p0 = layers[0]["p"]
+        for r in (0.125, 0.25, 0.5, 0.75, 1.0):
+            kk = J.topk_count(r, nkb)
+            for nn in (1, 8):
+                memory_sweep.append({
+                    "keep": r, "n_segments": nn, "kept_tokens": B * kk * blk,
+                    "saved_activation_mib": round((B * kk * blk * Hq * (es * D + 4) + B * nkb * 4) / 2**20, 2),
+                    "bwd_transient_mib": round(J.workspace_bytes(p0, J.JENGA_OP_BWD, kk, nn) / 2**20, 2)})
+
     # ---------------- CPU baseline: the oracle on a bounded sample of the same workload ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -517,6 +578,9 @@ def main():
         "kernel_avg_us": kernel_avg_us,
         "cpu_baseline": cpu,
         "memory": mem,
+        "memory_sweep": memory_sweep,
+        "step_evidence": step_evidence,
+        "scattered_kept": scattered,
         "input_gen_s": round(gen_s, 1),
     }
     if copy_ms is not None:
