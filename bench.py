@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 bf16 flop/clk/CU x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
 KERNELS = ("k_slse64", "k_smass64", "k_eq2_tiles", "k_eq2_reduce", "k_select", "k_pack_tp",
-           "k_fwd64", "k_prep64", "k_dkdv32", "k_dq64", "k_proj_gather", "k_proj_scatter",
+           "k_fwd64", "k_prep64", "k_bwd64", "k_proj_gather", "k_proj_scatter",
            "k_proj_logits", "k_ce_rows", "k_proj_dh", "k_mlp_act_gated", "k_mlp_block",
            "k_proj_gather_scatter")
 METRIC = "fwd+bwd token-sparse attn TFLOP/s (kept FLOPs) & tokens/s at S=32K; % MFMA peak"
@@ -54,7 +54,7 @@ def parse():
     return ap.parse_args()
 
 
-# The sources the dominant kernel (k_dkdv32) is compiled from: its traffic counters stay valid
+# The sources the dominant kernel (k_bwd64) is compiled from: its traffic counters stay valid
 # while these are unchanged.
 ROOFLINE_SOURCES = ("attn64.hip", "tiles64.h", "common.h", "kernels.h")
 
@@ -89,7 +89,7 @@ def _short(name: str) -> str:
 
 def summarize(trace_dir, fetch_dir, write_dir, bench_log, cfg_name="c5"):
     """Write profiles/kernels_<cfg>.md (rocprofv3 kernel-trace stats next to the bench's own
-    HIP-event averages) and profiles/traffic_k_dkdv32_<cfg>.json (HBM bytes per launch from
+    HIP-event averages) and profiles/traffic_k_bwd64_<cfg>.json (HBM bytes per launch from
     FETCH_SIZE / WRITE_SIZE, each scaled by the ratio known bytes / counter of the calibration
     copy, which moves exactly 1 GiB each way)."""
     import csv
@@ -143,7 +143,7 @@ def summarize(trace_dir, fetch_dir, write_dir, bench_log, cfg_name="c5"):
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"kernels_{cfg_name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    k = "k_dkdv32"
+    k = "k_bwd64"
     t = {"kernel": k, "config": cfg_name, "kernel_source_hash": kernel_source_hash(),
          "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4),
          "fetch_bytes_per_launch": round(fetch[k][1] / fetch[k][0] * f_fac),
@@ -295,32 +295,33 @@ def main():
     tflops = (fwd_flop + bwd_flop) / (attn_ms * 1e-3) / 1e12
     score_flop = 2 * 2.0 * D * Hq * B * L * S * (S + 1) / 2
 
-    # dominant attention kernel: k_dkdv32 (the dK/dV half of the backward), timed by the
-    # library's own HIP events on the stream it runs on, over the timed steps above.  Its
-    # algorithmic work is four 2*D contractions per (query head, causal kept pair): the score
-    # recompute, dP, dV and dK.
+    # dominant attention kernel: k_bwd64 (one launch per backward segment, running the dK/dV
+    # and dQ tiles of the segment), timed by the library's own HIP events on the stream it runs
+    # on, over the timed steps above.  Its algorithmic work is seven 2*D contractions per (query
+    # head, causal kept pair): the dK/dV tiles recompute the scores and form dP, dV and dK; the
+    # dQ tiles recompute the scores and dP and form dQ.
     kern_ms = {}
     for name in KERNELS:
         n, t = J.timing_query(name)
         if n:
             kern_ms[name] = (n, t)
-    n_dkdv, t_dkdv = kern_ms.get("k_dkdv32", (0, 0.0))
+    n_bwd, t_bwd = kern_ms.get("k_bwd64", (0, 0.0))
     roofline = None
-    if n_dkdv:
-        dkdv_flop_launch = 8.0 * D * Hq * pairs * K / n_dkdv
-        avg_ms = t_dkdv / n_dkdv
-        achieved = dkdv_flop_launch / (avg_ms * 1e-3) / 1e12
+    if n_bwd:
+        bwd_flop_launch = 14.0 * D * Hq * pairs * K / n_bwd
+        avg_ms = t_bwd / n_bwd
+        achieved = bwd_flop_launch / (avg_ms * 1e-3) / 1e12
         traffic = None
-        tfile = os.path.join(ROOT, "profiles", f"traffic_k_dkdv32_{args.config}.json")
+        tfile = os.path.join(ROOT, "profiles", f"traffic_k_bwd64_{args.config}.json")
         if os.path.exists(tfile) and args.kept == "selected" and nseg == cfg.n_segments:
             with open(tfile) as f:
                 tj = json.load(f)
             if tj.get("kernel_source_hash") == kernel_source_hash():
                 traffic = tj.get("hbm_bytes_per_launch")
-        roofline = {"kernel": "k_dkdv32", "bound": "mfma", "achieved": round(achieved, 2),
+        roofline = {"kernel": "k_bwd64", "bound": "mfma", "achieved": round(achieved, 2),
                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                    "algorithmic_flop_per_launch": dkdv_flop_launch, "launches": n_dkdv,
+                    "algorithmic_flop_per_launch": bwd_flop_launch, "launches": n_bwd,
                     "avg_launch_us": round(avg_ms * 1e3, 2)}
     kernel_avg_us = {kk: {"launches": n, "avg_us": round(1e3 * t / n, 2)} for kk, (n, t) in kern_ms.items()}
 

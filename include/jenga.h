@@ -336,8 +336,9 @@ int jenga_lm_head_ce_segmented(const jenga_loss_problem* p, const void* h, const
  * jenga_timing_enable(1) discards earlier records and, from then on, brackets every kernel
  * launched by the entry points above with two HIP events recorded on that call's stream;
  * jenga_timing_enable(0) stops recording (the records stay readable).  Kernel names:
- * k_slse64, k_smass64 (bf16 scoring), k_eq2_tiles, k_eq2_reduce (Eq. 2 scoring), k_select, k_pack_tp, k_fwd64, k_prep64, k_dkdv32,
- * k_dq64 (bf16 attention), k_proj_gather, k_proj_scatter, k_proj_gather_scatter,
+ * k_slse64, k_smass64 (bf16 scoring), k_eq2_tiles, k_eq2_reduce (Eq. 2 scoring), k_select,
+ * k_pack_tp, k_fwd64, k_prep64, k_bwd64 (bf16 attention; k_bwd64 is one launch per backward
+ * segment, with the dK/dV and dQ tiles), k_proj_gather, k_proj_scatter, k_proj_gather_scatter,
  * k_mlp_act_gated, k_mlp_act_relu, k_mlp_block (MLP elimination), k_proj_logits, k_ce_rows,
  * k_proj_dh (loss).  The fp32 kernels are not bracketed.
  *

@@ -139,7 +139,7 @@ def test_workspace_scales_with_segments_and_kept_blocks(J):
 def test_timing_calls_without_gpu_work(J):
     assert J.lib.jenga_timing_enable(2) == J.JENGA_ERR_INVALID_ARG
     J.timing_enable(True)
-    assert J.timing_query("k_dkdv32") == (0, 0.0)          # nothing launched yet
+    assert J.timing_query("k_bwd64") == (0, 0.0)           # nothing launched yet
     J.timing_enable(False)
     n = ctypes.c_int32(0)
     assert J.lib.jenga_timing_query(None, ctypes.byref(n), None) == J.JENGA_ERR_INVALID_ARG

@@ -13,8 +13,9 @@
 //   k_pack_tp   kept rows of K / V / Q (head h) -> TP tiles [D][32] in a workspace
 //   k_fwd64     forward:   S^T = K Q^T, online softmax per query (lane-local), O^T += V^T P^T
 //   k_prep64    backward prologue per segment: D_i = dO_i.O_i, dOut -> bf16 natural + TP
-//   k_dkdv32    key-major:   S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q
-//   k_dq64      query-major: S^T = K Q^T, dP^T = V dO^T, dQ += dS K   (no atomics)
+//   k_bwd64     one launch per segment with two kinds of workgroup tiles (no atomics):
+//                 dK/dV, key-major:   S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q
+//                 dQ, query-major:    S^T = K Q^T, dP^T = V dO^T, dQ += dS K
 #include "common.h"
 #include "kernels.h"
 #include "tiles64.h"
@@ -343,26 +344,31 @@ __global__ __launch_bounds__(256) void k_prep64(BwdParams p) {
 // of S = Q K^T), so a wave stays within 256 registers and two waves share each SIMD.
 // ------------------------------------------------------------------------------------------
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p) {
+struct DkdvLds {
   using C = T64<D>;
-  constexpr int KEYS = 32 * NW;
-  __shared__ __attribute__((aligned(1024))) char sK[NW * C::NAT32];
-  constexpr int OFF_Q = 0, OFF_DO = C::NAT32, OFF_QT = 2 * C::NAT32, OFF_DOT = 2 * C::NAT32 + C::TP32;
-  constexpr int OFF_LD = 2 * C::NAT32 + 2 * C::TP32;            // lse2[32], D[32] (fp32)
-  constexpr int STAGE = OFF_LD + 256;
-  __shared__ __attribute__((aligned(1024))) char sA[STAGE];
-  __shared__ __attribute__((aligned(1024))) char sB[STAGE];
-  __shared__ int ktab[kKeptTab];
+  static constexpr int OFF_Q = 0, OFF_DO = C::NAT32, OFF_QT = 2 * C::NAT32, OFF_DOT = 2 * C::NAT32 + C::TP32;
+  static constexpr int OFF_LD = 2 * C::NAT32 + 2 * C::TP32;     // lse2[32], D[32] (fp32)
+  static constexpr int STAGE = OFF_LD + 256;
+  static constexpr int KROWS = NW * C::NAT32;                   // the workgroup's K rows
+};
 
-  const Tile3 tl = xcd_tile();
-  const int b = tl.z, g = tl.y;
+// key tile tx (32 * NW kept keys) of KV head g, batch row b
+template <int D, int NW>
+__device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB, char* sK, int* ktab,
+                                          int tx, int g, int b) {
+  using C = T64<D>;
+  using LY = DkdvLds<D, NW>;
+  constexpr int KEYS = 32 * NW;
+  constexpr int OFF_Q = LY::OFF_Q, OFF_DO = LY::OFF_DO, OFF_QT = LY::OFF_QT, OFF_DOT = LY::OFF_DOT;
+  constexpr int OFF_LD = LY::OFF_LD;
+
   const int G = p.Hq / p.Hkv;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
   const int32_t* kept = p.kept + (int64_t)b * p.nkb;
   const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
   const int qs = p.seg * p.seg_len;
   const int qe = min(qs + p.seg_len, Nk);
-  const int k0 = tl.x * KEYS;
+  const int k0 = tx * KEYS;
   if (qs >= qe || k0 >= qe) return;
   const int kw0 = k0 + 32 * w;
   const bool key_valid = kw0 < Nk;                               // Nk is a multiple of 64
@@ -452,6 +458,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
     const float* lsel = (const float*)(buf + OFF_LD);
     const float* Dl = lsel + 32;
     f32x16 sacc = zero16(), pacc = zero16();
+    const char* Kw = sK + w * C::NAT32;                          // this wave's 32 key rows
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
       sacc = Mfma<bf16>::mma(ldo(Ql, rp.nat[s]), ldo(Kw, rp.nat[s]), sacc);
@@ -543,21 +550,25 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_dkdv32(BwdParams p
 // dQ: query-major.  Workgroup = NW waves x 32 kept queries of one query head (NW = 8: the K, V
 // and K-transposed tiles of a step serve 256 queries; two waves per SIMD either way).
 // ------------------------------------------------------------------------------------------
+template <int D>
+struct DqLds {
+  using C = T64<D>;
+  static constexpr int OFF_K = 0, OFF_V = C::NAT32, OFF_KT = 2 * C::NAT32;
+  static constexpr int STAGE = 2 * C::NAT32 + C::TP32;
+};
+
+// query tile tx (32 * NB * NW kept queries of the segment, counted from its end) of query
+// head h, batch row b
 template <int D, int NB, int NW>
-__global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) {
+__device__ __forceinline__ void dq_tile(const BwdParams& p, char* sA, char* sB, char* sC, int* ktab,
+                                        int tx, int h, int b) {
   constexpr int RW = 32 * NB, RG = RW * NW;
   using C = T64<D>;
-  constexpr int OFF_K = 0, OFF_V = C::NAT32, OFF_KT = 2 * C::NAT32;
-  constexpr int STAGE = 2 * C::NAT32 + C::TP32;
+  constexpr int OFF_K = DqLds<D>::OFF_K, OFF_V = DqLds<D>::OFF_V, OFF_KT = DqLds<D>::OFF_KT;
+  constexpr int STAGE = DqLds<D>::STAGE;
   using DC = DmaCount<D, NW>;
   constexpr int PER = 2 * DC::NAT_W + DC::TP_W;  // direct-to-LDS instructions per wave per step
-  __shared__ __attribute__((aligned(1024))) char sA[STAGE];
-  __shared__ __attribute__((aligned(1024))) char sB[STAGE];
-  __shared__ __attribute__((aligned(1024))) char sC[STAGE];
-  __shared__ int ktab[kKeptTab];
 
-  const Tile3 tl = xcd_tile();
-  const int b = tl.z, h = tl.y;
   const int g = h / (p.Hq / p.Hkv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
   const int32_t* kept = p.kept + (int64_t)b * p.nkb;
@@ -565,8 +576,8 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
   const int qs = p.seg * p.seg_len;
   const int qe = min(qs + p.seg_len, Nk);
   const int nqt = (qe - qs + RG - 1) / RG;
-  if (qs >= qe || tl.x >= nqt) return;
-  const int q0 = qs + (nqt - 1 - tl.x) * RG;                    // heaviest tiles first
+  if (qs >= qe || tx >= nqt) return;
+  const int q0 = qs + (nqt - 1 - tx) * RG;                      // heaviest tiles first
   const int qw0 = q0 + RW * w;
   const bool active = qw0 < qe;                                  // qe - qs multiple of 64
   const int qlast = min(q0 + RG, qe) - 1;
@@ -716,6 +727,53 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_dq64(BwdParams p) 
 constexpr int FWD_NB = 1, FWD_NW = 4;
 constexpr int DKDV_NW = 8;
 constexpr int DQ_NB = 1, DQ_NW = 8;
+static_assert(DKDV_NW == DQ_NW, "the fused backward launch runs both tile kinds in one workgroup shape");
+
+// ------------------------------------------------------------------------------------------
+// One segment's dQ tiles and dK/dV tiles in one launch.  Each kind alone fills the GPU with
+// one workgroup per compute unit, so a launch lasts as long as its heaviest tile (the causal
+// tiles vary up to 8x in work); run together, short tiles fill in behind long ones.
+//
+// The launch is two runs of workgroups, each a multiple of 8 long (idle workgroups pad them):
+// the dQ tiles, heaviest first (their queries see every earlier key), then the dK/dV tiles.
+// Within a run, XCD x (launch index mod 8) takes a contiguous range of tiles in launch order,
+// so the tiles of one head share an L2, as in xcd_tile().
+//
+// The LDS buffers are separate arrays, shared by the two kinds (dQ: A, B, C; dK/dV: A, B and
+// the K rows): as distinct objects the compiler can tell that a direct-to-LDS load into one
+// buffer does not write another, and waits only for the loads of the buffer it reads.
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64 * DQ_NW, 2) void k_bwd64(BwdParams pq, BwdParams pk, BwdGrid gr) {
+  using KL = DkdvLds<D, DKDV_NW>;
+  using QL = DqLds<D>;
+  constexpr int AB = KL::STAGE > QL::STAGE ? KL::STAGE : QL::STAGE;
+  __shared__ __attribute__((aligned(1024))) char bufA[AB];
+  __shared__ __attribute__((aligned(1024))) char bufB[AB];
+  __shared__ __attribute__((aligned(1024))) char bufC[QL::STAGE];
+  __shared__ __attribute__((aligned(1024))) char bufK[KL::KROWS];
+  __shared__ int ktab[kKeptTab];
+  // pq and pk are the same parameters, one copy per tile kind: a field that both kinds read
+  // would otherwise be loaded once before the branch and held in scalar registers through
+  // either body, more than the two bodies need on their own
+  const int lin = blockIdx.x;
+  // run [o, o + n rounded up to 8): XCD i & 7 takes tiles (i & 7) * q .. + q - 1, q = pad / 8
+  auto tile_of = [&](int o, int n) {
+    const int i = lin - o, q = ((n + 7) >> 3);
+    return (i & 7) * q + (i >> 3);
+  };
+  if (lin < gr.o_kv) {
+    const int L = tile_of(0, gr.n_dq);
+    if (L >= gr.n_dq) return;
+    dq_tile<D, DQ_NB, DQ_NW>(pq, bufA, bufB, bufC, ktab, L % gr.nqt, (L / gr.nqt) % pq.Hq,
+                             L / (gr.nqt * pq.Hq));
+  } else {
+    const int L = tile_of(gr.o_kv, gr.n_kv);
+    if (L >= gr.n_kv) return;
+    dkdv_tile<D, DKDV_NW>(pk, bufA, bufB, bufK, ktab, L % gr.nkt, (L / gr.nkt) % pk.Hkv,
+                          L / (gr.nkt * pk.Hkv));
+  }
+}
 
 template <int D>
 static hipError_t launch_fwd64_t(const FwdParams& p, hipStream_t st) {
@@ -761,16 +819,17 @@ static hipError_t bwd64_segment_t(const BwdParams& p, hipStream_t st) {
   e = pack_tp<D>(a, p.B, st);
   if (e != hipSuccess) return e;
   const int seg_end = p.seg * L + seg_cap;
-  constexpr int KG = 32 * DKDV_NW;
-  {
-    TimedLaunch tl("k_dkdv32", st);
-    k_dkdv32<D, DKDV_NW><<<dim3((seg_end + KG - 1) / KG, p.Hkv, p.B), 64 * DKDV_NW, 0, st>>>(p);
-    e = hipGetLastError();
-  }
-  if (e != hipSuccess) return e;
-  constexpr int QG = 32 * DQ_NB * DQ_NW;
-  TimedLaunch tl("k_dq64", st);
-  k_dq64<D, DQ_NB, DQ_NW><<<dim3((seg_cap + QG - 1) / QG, p.Hq, p.B), 64 * DQ_NW, 0, st>>>(p);
+  constexpr int KG = 32 * DKDV_NW, QG = 32 * DQ_NB * DQ_NW;
+  auto pad8 = [](int n) { return (n + 7) & ~7; };
+  BwdGrid gr;
+  gr.nqt = (seg_cap + QG - 1) / QG;
+  gr.nkt = (seg_end + KG - 1) / KG;
+  gr.n_dq = gr.nqt * p.Hq * p.B;
+  gr.n_kv = gr.nkt * p.Hkv * p.B;
+  gr.o_kv = pad8(gr.n_dq);
+  const int nwg = gr.o_kv + pad8(gr.n_kv);
+  TimedLaunch tl("k_bwd64", st);
+  k_bwd64<D><<<dim3(nwg), 64 * DQ_NW, 0, st>>>(p, p, gr);
   return hipGetLastError();
 }
 

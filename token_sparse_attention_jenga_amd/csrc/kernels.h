@@ -106,6 +106,15 @@ struct BwdParams {
   float scale, scale_log2;
 };
 
+// Workgroup runs of the fused backward launch of one segment (computed on the host): the dQ
+// tiles, then the dK/dV key tiles; o_kv is the launch offset of the second run (a multiple of 8).
+struct BwdGrid {
+  int nqt, nkt;                // dQ tiles per query head; dK/dV key tiles per KV head
+  int n_dq, n_kv;              // workgroups of each run (all heads and batch rows)
+  int o_kv;
+};
+
+
 // dtype: 0 = fp32 operands, 1 = bf16 operands.  Each returns hipGetLastError().
 hipError_t launch_score(const ScoreParams& p, int dtype, int D, hipStream_t st);
 hipError_t launch_select(const SelectParams& p, hipStream_t st);
