@@ -127,12 +127,12 @@ def test_workspace_scales_with_segments_and_kept_blocks(J):
     w1 = J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 1)
     w8 = J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 8)
     w8_half = J.workspace_bytes(p, J.JENGA_OP_BWD, 64, 8)
-    ktp = 32 * 128 * 128 * 128 * 2                # transposed K tiles: all kept keys
+    vtp = 32 * 128 * 128 * 128 * 2                # forward: transposed V tiles of all kept keys
     seg = lambda L: 2 * 32 * L * 4 + 3 * 32 * L * 128 * 2   # D, lse2, dOut, dOut^T and Q^T tiles
-    assert w1 == ktp + seg(16384)
-    assert w8 == ktp + seg(2048)                  # the per-segment part shrinks as 1/N
-    assert abs(w8_half * 2 - w8) <= 4096          # everything scales with the kept tokens
-    assert J.workspace_bytes(p, J.JENGA_OP_FWD, 128) == ktp
+    assert w1 == seg(16384)
+    assert w8 == seg(2048)                        # the backward workspace shrinks as 1/N
+    assert abs(w8_half * 2 - w8) <= 4096          # and scales with the kept tokens
+    assert J.workspace_bytes(p, J.JENGA_OP_FWD, 128) == vtp
     assert J.workspace_bytes(_problem(J), J.JENGA_OP_FWD, 8) == 0       # fp32 path needs none
 
 

@@ -56,23 +56,22 @@ int seg_len_of(int ncap, int n_segments) {
 }
 
 struct BwdLayout {
-  size_t d, l2, dO, ktp, qtp, dotp, total;
+  size_t d, l2, dO, qtp, dotp, total;
 };
 
 BwdLayout bwd_layout(const jenga_problem* p, int max_kept_blocks, int n_segments) {
   const int ncap = max_kept_blocks * p->block;
   const int L = seg_len_of(ncap, n_segments);
   const size_t es = p->dtype == JENGA_DTYPE_BF16 ? 2 : 4;
-  const size_t B = p->batch, Hq = p->n_heads_q, Hkv = p->n_heads_kv, D = p->head_dim;
+  const size_t B = p->batch, Hq = p->n_heads_q, D = p->head_dim;
   BwdLayout o;
   o.d = 0;
   o.l2 = o.d + align_up(B * Hq * L * sizeof(float));
   o.dO = o.l2 + (p->dtype == JENGA_DTYPE_BF16 ? align_up(B * Hq * L * sizeof(float)) : 0);
   size_t end = o.dO + align_up(B * L * Hq * D * es);
-  o.ktp = o.qtp = o.dotp = end;
+  o.qtp = o.dotp = end;
   if (p->dtype == JENGA_DTYPE_BF16) {            // transposed operand tiles of the bf16 path
-    o.ktp = end;
-    o.qtp = o.ktp + align_up(B * Hkv * (size_t)ncap * D * 2);
+    o.qtp = end;
     o.dotp = o.qtp + align_up(B * Hq * (size_t)L * D * 2);
     end = o.dotp + align_up(B * Hq * (size_t)L * D * 2);
   }
@@ -408,7 +407,6 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
   bp.wsD = (float*)((char*)workspace + lay.d);
   bp.wsL2 = (float*)((char*)workspace + lay.l2);
   bp.wsdO = (char*)workspace + lay.dO;
-  bp.ktp = (char*)workspace + lay.ktp;
   bp.qtp = (char*)workspace + lay.qtp;
   bp.dotp = (char*)workspace + lay.dotp;
   bp.B = p->batch;
@@ -423,8 +421,6 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
   bp.scale = scale_of(p);
   bp.scale_log2 = bp.scale * 1.4426950408889634f;
   const bool fast = p->dtype == JENGA_DTYPE_BF16;
-  if (fast && jenga::launch_bwd64_pack_keys(bp, p->head_dim, (hipStream_t)stream) != hipSuccess)
-    return JENGA_ERR_LAUNCH;
   for (int s = 0; s < n_segments; ++s) {
     if ((int64_t)s * L >= ncap) break;
     bp.seg = s;

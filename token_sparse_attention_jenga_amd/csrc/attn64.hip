@@ -553,8 +553,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB
 template <int D>
 struct DqLds {
   using C = T64<D>;
-  static constexpr int OFF_K = 0, OFF_V = C::NAT32, OFF_KT = 2 * C::NAT32;
-  static constexpr int STAGE = 2 * C::NAT32 + C::TP32;
+  static constexpr int OFF_K = 0, OFF_V = C::NAT32;
+  static constexpr int STAGE = 2 * C::NAT32;
 };
 
 // query tile tx (32 * NB * NW kept queries of the segment, counted from its end) of query
@@ -564,10 +564,10 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, char* sA, char* sB, 
                                         int tx, int h, int b) {
   constexpr int RW = 32 * NB, RG = RW * NW;
   using C = T64<D>;
-  constexpr int OFF_K = DqLds<D>::OFF_K, OFF_V = DqLds<D>::OFF_V, OFF_KT = DqLds<D>::OFF_KT;
+  constexpr int OFF_K = DqLds<D>::OFF_K, OFF_V = DqLds<D>::OFF_V;
   constexpr int STAGE = DqLds<D>::STAGE;
   using DC = DmaCount<D, NW>;
-  constexpr int PER = 2 * DC::NAT_W + DC::TP_W;  // direct-to-LDS instructions per wave per step
+  constexpr int PER = 2 * DC::NAT_W;             // direct-to-LDS instructions per wave per step
 
   const int g = h / (p.Hq / p.Hkv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
@@ -617,21 +617,19 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, char* sA, char* sB, 
   const char* kbase = (const char*)((const bf16*)p.k + b * p.ks[0] + g * p.ks[2]);
   const char* vbase = (const char*)((const bf16*)p.v + b * p.vs[0] + g * p.vs[2]);
   const int64_t kstride = p.ks[1] * 2, vstride = p.vs[1] * 2;
-  const char* ktp = (const char*)p.ktp + (((int64_t)b * p.Hkv + g) * (p.ncap / 32)) * C::TP32;
   NatPlan<D, NW> kplan, vplan;
   kplan.init(kstride);
   vplan.init(vstride);
-  TpPlan<D, NW> tplan;
-  tplan.init();
   ReadPlan<D> rp;
   rp.init();
+  TrPlan<D> tp;
+  tp.init();
 
-  const rsrc_t rk = make_rsrc(kbase), rv = make_rsrc(vbase), rkt = make_rsrc(ktp);
+  const rsrc_t rk = make_rsrc(kbase), rv = make_rsrc(vbase);
   auto issue = [&](int step, char* buf) {
     const int pos0 = kt.pos_u(step * 32);
     kplan.issue(buf + OFF_K, rk, (uint32_t)(pos0 * kstride));
     vplan.issue(buf + OFF_V, rv, (uint32_t)(pos0 * vstride));
-    tplan.issue(buf + OFF_KT, rkt, (uint32_t)(step * C::TP32));
   };
 
   auto compute = [&](int step, const char* buf) {
@@ -639,7 +637,6 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, char* sA, char* sB, 
     if (!active || kr0 > qw0 + RW - 1) return;
     const char* Kl = buf + OFF_K;
     const char* Vl = buf + OFF_V;
-    const char* KTl = buf + OFF_KT;
     f32x16 st[NB], dp[NB];
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
@@ -677,12 +674,12 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, char* sA, char* sB, 
       for (int qb = 0; qb < NB; ++qb) af[qb] = frag_from_acc(st[qb], j);
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
-        const bf16x8 bk = ldo(KTl + db * 2048, rp.tp[j]);
+        const bf16x8 bk = ldtr(Kl + j * 16 * C::ROWB, tp.off[0][db], tp.off[1][db]);
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb) acc[qb][db] = Mfma<bf16>::mma(af[qb], bk, acc[qb][db]);
       }
     }
-    SCHED_READS_AHEAD(2 * C::NDB, 1, NB, 1);
+    SCHED_READS_AHEAD(2 * C::NDB, 2, NB, 1);
   };
 
   auto stage = [&](int t, const char* cur, char* nxt) {
@@ -789,17 +786,6 @@ static hipError_t launch_fwd64_t(const FwdParams& p, hipStream_t st) {
 
 hipError_t launch_fwd64(const FwdParams& p, int D, hipStream_t st) {
   return D == 64 ? launch_fwd64_t<64>(p, st) : launch_fwd64_t<128>(p, st);
-}
-
-template <int D>
-static hipError_t pack_keys_t(const BwdParams& p, hipStream_t st) {
-  PackArgs a{p.k, p.ks[0], p.ks[1], p.ks[2], p.kept, p.n_kept, p.block, p.nkb, p.max_kept_blocks,
-             0, p.ncap, p.ncap / 32, p.Hkv, p.ktp};
-  return pack_tp<D>(a, p.B, st);
-}
-
-hipError_t launch_bwd64_pack_keys(const BwdParams& p, int D, hipStream_t st) {
-  return D == 64 ? pack_keys_t<64>(p, st) : pack_keys_t<128>(p, st);
 }
 
 template <int D>

@@ -99,7 +99,6 @@ struct BwdParams {
   float* wsD;    // [B][Hq][L]   dot(dO, O) of the segment's queries
   float* wsL2;   // bf16 path: [B][Hq][L] lse of the segment's queries in the log2 domain
   void* wsdO;    // [B][L][Hq][D] dOut rows of the segment in operand dtype, by kept rank
-  void* ktp;     // bf16 path: [B][Hkv][ncap/32] TP tiles of the kept K rows
   void* qtp;     // bf16 path: [B][Hq][L/32] TP tiles of the segment's Q rows
   void* dotp;    // bf16 path: [B][Hq][L/32] TP tiles of the segment's dOut rows (bf16)
   int B, S, Hq, Hkv, block, nkb, max_kept_blocks, ncap, seg_len, seg;
@@ -155,7 +154,6 @@ hipError_t timing_query(const char* name, int* launches, double* total_ms);
 
 // bf16 attention kernels (attn64.hip)
 hipError_t launch_fwd64(const FwdParams& p, int D, hipStream_t st);
-hipError_t launch_bwd64_pack_keys(const BwdParams& p, int D, hipStream_t st);
 hipError_t launch_bwd64_segment(const BwdParams& p, int D, hipStream_t st);
 
 }  // namespace jenga

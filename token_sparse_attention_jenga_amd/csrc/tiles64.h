@@ -22,6 +22,16 @@ namespace jenga {
 
 __host__ __device__ constexpr int pi16(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
+// Natural-tile swizzle: chunk c of row r is stored at chunk c ^ natswz(r).  A bijection on
+// r % CPR, so 16 consecutive rows read at one logical chunk hit 16 distinct chunks.  With
+// 16 chunks per row the two low row bits go to the two high chunk bits: a transposing read
+// (four consecutive rows x four consecutive chunks per 32 lanes) then also covers all 16 chunk
+// positions, i.e. all 64 banks.
+template <int CPR>
+__host__ __device__ constexpr int natswz(int r) {
+  return CPR == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (r & (CPR - 1));
+}
+
 template <int D>
 struct T64 {
   static constexpr int ROWB = D * 2;       // natural row bytes
@@ -150,7 +160,7 @@ struct NatPlan {
     for (int i = 0; i < MAXW; ++i) {
       const int idx = (w + i * NW) * 64 + l;
       const int row = idx / CPR, phys = idx % CPR;
-      off[i] = (uint32_t)(row * row_stride) + ((phys ^ (row & (CPR - 1))) << 4);
+      off[i] = (uint32_t)(row * row_stride) + ((phys ^ natswz<CPR>(row)) << 4);
     }
   }
   // rows at byte offset soff (row 0) from the resource's base
@@ -198,13 +208,46 @@ struct ReadPlan {
     const int l = threadIdx.x & 63, hl = l >> 5, lc = l & 31;
     constexpr int CPR = T64<D>::CPR;
 #pragma unroll
-    for (int s = 0; s < T64<D>::NS; ++s) nat[s] = lc * T64<D>::ROWB + (((2 * s + hl) ^ (lc & (CPR - 1))) << 4);
+    for (int s = 0; s < T64<D>::NS; ++s) nat[s] = lc * T64<D>::ROWB + (((2 * s + hl) ^ natswz<CPR>(lc)) << 4);
 #pragma unroll
     for (int j = 0; j < 2; ++j) tp[j] = lc * 64 + (((2 * j + hl) ^ tpswz(lc)) << 4);
   }
 };
 
 __device__ inline bf16x8 ldo(const char* tile, int off) { return *(const bf16x8*)(tile + off); }
+
+// Per-lane LDS offsets for an operand whose reduction runs down the rows of a natural tile (the
+// transposed operand of a 32x32x16 product), read with two transposing 8-byte reads.  The
+// operand pairs with a 32x32 accumulator's registers 8j..8j+7 as the other operand, whose
+// reduction index i = 0..7 of lane half h is row 16j + pi16(8h + i): rows 16j + 4h + 0..3
+// (first read, t = 0) and 16j + 8 + 4h + 0..3 (second read, t = 1).  Lane l's column is
+// 32 db + l % 32.  Within a 16-lane group, lane s addresses row R + s/4 at column
+// C + 4 (s % 4), and receives rows R..R+3 of column C + s.  k-step j adds 16 j rows, which
+// leave the swizzle unchanged: a constant j * 16 * ROWB.
+template <int D>
+struct TrPlan {
+  int off[2][T64<D>::NDB];
+  __device__ void init() {
+    constexpr int CPR = T64<D>::CPR, ROWB = T64<D>::ROWB;
+    const int l = threadIdx.x & 63, hl = l >> 5, s = l & 15, grp = (l >> 4) & 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < T64<D>::NDB; ++db) {
+        const int row = 8 * t + 4 * hl + (s >> 2);
+        const int col = 32 * db + 16 * grp + 4 * (s & 3);
+        off[t][db] = row * ROWB + (((col >> 3) ^ natswz<CPR>(row)) << 4) + (col & 7) * 2;
+      }
+  }
+};
+
+__device__ inline bf16x8 ldtr(const char* tile, int off0, int off1) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + off0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + off1));
+  const s16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, c);
+}
 
 // Kept-block table staged in LDS once per workgroup, so the hot loops resolve a kept rank to
 // its token position without a global-memory round trip.  Blocks beyond the table's capacity
