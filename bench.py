@@ -55,17 +55,22 @@ def parse():
 
 
 # The sources the dominant kernel (k_bwd64) is compiled from: its traffic counters stay valid
-# while these are unchanged.
+# while their code is unchanged (comments and layout do not count).
 ROOFLINE_SOURCES = ("attn64.hip", "tiles64.h", "common.h", "kernels.h")
 
 
 def kernel_source_hash() -> str:
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "token_sparse_attention_jenga_amd", "csrc")
     for name in ROOFLINE_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+        with open(os.path.join(csrc, name)) as f:
+            code = f.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)     # block comments
+        code = re.sub(r"//[^\n]*", " ", code)                    # line comments
+        code = " ".join(code.split())                            # layout
+        h.update(name.encode())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 
@@ -114,7 +119,8 @@ def summarize(trace_dir, fetch_dir, write_dir, bench_log, cfg_name="c5"):
              "    cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              "-d <repo>/gpurun_out/prof_trace -o run -- python3 <repo>/bench.py --steps 2 --warmup 1 "
              "--no-cpu-baseline", "",
-             f"Kernel source hash {kernel_source_hash()}.  Columns: rocprofv3 calls / average / total "
+             f"Kernel source hash {kernel_source_hash()} (code of the kernel sources, comments and "
+             "layout excluded).  Columns: rocprofv3 calls / average / total "
              "over warmup + timed steps; the bench's own HIP-event average over the timed steps.", "",
              "| kernel | calls | rocprof avg us | rocprof total ms | % | bench event avg us |",
              "|---|---|---|---|---|---|"]

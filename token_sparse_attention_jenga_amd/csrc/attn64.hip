@@ -6,11 +6,12 @@
 //
 // Every wave owns 32 rows (one 32x32 MFMA block); waves of a workgroup share K / V / Q / dO
 // tiles that direct-to-LDS loads stage through a ring of LDS buffers while earlier tiles are
-// consumed.  Every MFMA operand is one 16-byte LDS read: operands that reduce over head_dim come
-// from natural tiles; operands that reduce over rows come from TP tiles prepared in global memory
-// (see tiles64.h), so no transpose happens inside the hot loops.
+// consumed.  Operands that reduce over head_dim are 16-byte reads of natural tiles.  Operands
+// that reduce over rows are 16-byte reads of TP tiles prepared in global memory (V in the
+// forward, Q and dO in the dK/dV tiles), or, in the dQ tiles, two transposing 8-byte reads of
+// the natural K tile (see tiles64.h).
 //
-//   k_pack_tp   kept rows of K / V / Q (head h) -> TP tiles [D][32] in a workspace
+//   k_pack_tp   kept rows of V / Q (head h) -> TP tiles [D][32] in a workspace
 //   k_fwd64     forward:   S^T = K Q^T, online softmax per query (lane-local), O^T += V^T P^T
 //   k_prep64    backward prologue per segment: D_i = dO_i.O_i, dOut -> bf16 natural + TP
 //   k_bwd64     one launch per segment with two kinds of workgroup tiles (no atomics):

@@ -2,9 +2,10 @@
 //
 // Two LDS tile forms, both filled with gfx950 direct-to-LDS loads (global_load_lds_dwordx4:
 // lane i of a wave writes its 16 bytes at LDS base + 16*i, from any global address):
-//   natural tile  [32 rows][D] bf16, 16-byte chunk c of row r stored at chunk c ^ (r % CPR)
-//                 (CPR = chunks per row); read as MFMA operands whose reduction runs along
-//                 head_dim.
+//   natural tile  [32 rows][D] bf16, 16-byte chunk c of row r stored at chunk c ^ natswz(r)
+//                 (a bijection on r % CPR, CPR = chunks per row); read as MFMA operands whose
+//                 reduction runs along head_dim, or transposed (TrPlan) as operands whose
+//                 reduction runs down its rows.
 //   TP tile       [D][32 positions] bf16: row r of the source tile sits at position pi(r),
 //                 pi swapping bits 2 and 3 of r.  Chunk c of line d stored at c ^ tpswz(d).
 // Both swizzles make every 16-lane (and every 8-lane) group of a 16-byte read hit distinct
