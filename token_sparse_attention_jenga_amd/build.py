@@ -20,9 +20,9 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 
-# Per-file code generation options.  attn64.hip: MFMA results in the VGPR form, so the
-# 64-row-per-wave kernels keep their softmax accumulators in VGPRs and use the AGPR file for
-# the long-lived gradient accumulators instead of spilling to scratch.
+# Per-file code generation options.  attn64.hip: MFMA results in the VGPR form, where the
+# softmax and gradient VALU code reads them without copies; at two waves per SIMD the VGPR and
+# AGPR files are one 256-register budget per wave either way.
 EXTRA = {"attn64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

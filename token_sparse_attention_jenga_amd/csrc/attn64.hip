@@ -387,7 +387,6 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB
     for (int t = 0; t < NW; ++t)
       if (k0 + 32 * t < Nk) kp.issue(sK + t * C::NAT32, rkk, (uint32_t)(kt.pos_u(k0 + 32 * t) * kstride));
   }
-  const char* Kw = sK + w * C::NAT32;                            // this wave's 32 key rows
   bf16x8 vf[C::NS];
   if (key_valid) {
     const int pos = kt.pos(kw0 + lc);
@@ -566,7 +565,6 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, char* sA, char* sB, 
   constexpr int RW = 32 * NB, RG = RW * NW;
   using C = T64<D>;
   constexpr int OFF_K = DqLds<D>::OFF_K, OFF_V = DqLds<D>::OFF_V;
-  constexpr int STAGE = DqLds<D>::STAGE;
   using DC = DmaCount<D, NW>;
   constexpr int PER = 2 * DC::NAT_W;             // direct-to-LDS instructions per wave per step
 
