@@ -1,8 +1,8 @@
 """Edge cases of the attention path against the oracle ([notes] 4.4 permutation-free token
 movement, the segmented backward): a kept count above max_kept_blocks (only the first
 max_kept_blocks blocks take part), large blocks, a batch row with nothing kept beside one with
-blocks kept, segments past the kept count (empty), and bit-for-bit repeatable
-bf16 gradients."""
+blocks kept, segments past the kept count (empty), head counts whose tiles do not fill the
+launch evenly, and bit-for-bit repeatable bf16 gradients."""
 import numpy as np
 import pytest
 
@@ -105,3 +105,15 @@ def test_bf16_backward_repeatable(J):
     b = _run(J, q, k, v, x0, dout, kept, block, dtype, 3, maxk=8)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_odd_head_counts(J):
+    """Grouped heads whose tile counts are not multiples of 8: the backward launch pads each
+    of its two workgroup runs with idle workgroups, and every dQ and dK/dV tile must still be
+    computed exactly once."""
+    B, S, Hq, Hkv, D, block, dtype = 2, 768, 6, 3, 128, 64, "bf16"
+    q, k, v, x0, dout = random_inputs(B, S, Hq, Hkv, D, dtype, seed=26)
+    kept = [[0, 1, 4, 5, 7, 9, 10], [2, 3, 6, 11]]
+    say(f"odd heads: Hq {Hq} Hkv {Hkv}, kept {kept}, 3 segments")
+    got = _run(J, q, k, v, x0, dout, kept, block, dtype, 3, maxk=7)
+    _check(q, k, v, x0, dout, kept, block, got, tol_for(dtype))
