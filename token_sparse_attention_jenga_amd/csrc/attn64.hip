@@ -519,7 +519,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB
 
   if (!key_valid) return;
   // dK (scaled), dV += accumulators; lane holds head_dim column db*32 + lc of keys
-  // kw0 + 8(r/4) + 4hl + r%4.  Reads are batched per 4-register group.
+  // kw0 + 8(r/4) + 4hl + r%4.  Reads are batched per 4-register group.  The wave's 32 kept
+  // ranks lie in one kept block (blocks are multiples of 64 rows), so one lookup places them
+  // all: a lookup per row waited for every read issued before it.
+  const int kpos0 = kt.pos_u(kw0);
 #pragma unroll
   for (int rg = 0; rg < 4; ++rg) {
     float* dkr[4];
@@ -527,7 +530,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB
     float xk[4][C::NDB], xv[4][C::NDB];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int pos = kt.pos(kw0 + 8 * rg + 4 * hl + i);
+      const int pos = kpos0 + 8 * rg + 4 * hl + i;
       dkr[i] = p.dk + (((int64_t)b * p.S + pos) * p.Hkv + g) * D + lc;
       dvr[i] = p.dv + (((int64_t)b * p.S + pos) * p.Hkv + g) * D + lc;
 #pragma unroll
@@ -696,16 +699,18 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, char* sA, char* sB, 
   wait_all_mem();                                        // drain the trailing reloads
 
   if (!active) return;
-  // dQ accumulator: lane holds head_dim column db*32 + lc of queries 8(r/4)+4hl+r%4
+  // dQ accumulator: lane holds head_dim column db*32 + lc of queries 8(r/4)+4hl+r%4.  Each
+  // 32-rank group lies in one kept block: one lookup per group (see the dK/dV tile).
 #pragma unroll
   for (int qb = 0; qb < NB; ++qb) {
+    const int qpos0 = kt.pos_u(qw0 + 32 * qb);
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       float* dqr[4];
       float x[4][C::NDB];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int pos = kt.pos(qw0 + 32 * qb + 8 * rg + 4 * hl + i);
+        const int pos = qpos0 + 8 * rg + 4 * hl + i;
         dqr[i] = p.dq + (((int64_t)b * p.S + pos) * p.Hq + h) * D + lc;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) x[i][db] = dqr[i][db * 32];
