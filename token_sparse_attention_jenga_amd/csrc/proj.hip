@@ -206,6 +206,9 @@ __global__ __launch_bounds__(512, 1) void k_proj(ProjParams p) {
     for (int mb = 0; mb < 2; ++mb) {
       const int rb = r0 + 64 * wm + 32 * mb;
       if (rb >= Nk) continue;                              // Nk is a multiple of 32
+      // the 32 ranks rb.. lie in one kept block (blocks are multiples of 64 rows): one lookup
+      // places them all, where a lookup per row waited for every read issued before it
+      const int pos0 = (MODE == kScatter || MODE == kGatherScatter) ? kt.pos_u(rb) : 0;
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg)
 #pragma unroll
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(512, 1) void k_proj(ProjParams p) {
               float* orow = (float*)p.out + b * p.os0 + (int64_t)r * p.os1;
               orow[col] = v;
             } else {                                       // kScatter, kGatherScatter
-              float* orow = (float*)p.out + b * p.os0 + (int64_t)kt.pos(r) * p.os1;
+              float* orow = (float*)p.out + b * p.os0 + (int64_t)(pos0 + (r - rb)) * p.os1;
               orow[col] += v;
             }
           }
