@@ -519,33 +519,36 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB
 
   if (!key_valid) return;
   // dK (scaled), dV += accumulators; lane holds head_dim column db*32 + lc of keys
-  // kw0 + 8(r/4) + 4hl + r%4.  Reads are batched per 4-register group.  The wave's 32 kept
+  // kw0 + 8(r/4) + 4hl + r%4.  Reads are issued in two batches of 8 rows.  The wave's 32 kept
   // ranks lie in one kept block (blocks are multiples of 64 rows), so one lookup places them
   // all: a lookup per row waited for every read issued before it.
   const int kpos0 = kt.pos_u(kw0);
+  const int64_t rstride = (int64_t)p.Hkv * D;                     // elements per token row
+  float* const dk0 = p.dk + (((int64_t)b * p.S + kpos0 + 4 * hl) * p.Hkv + g) * D + lc;
+  float* const dv0 = p.dv + (((int64_t)b * p.S + kpos0 + 4 * hl) * p.Hkv + g) * D + lc;
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg) {
-    float* dkr[4];
-    float* dvr[4];
-    float xk[4][C::NDB], xv[4][C::NDB];
+  for (int half = 0; half < 2; ++half) {
+    float xk[8][C::NDB], xv[8][C::NDB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pos = kpos0 + 8 * rg + 4 * hl + i;
-      dkr[i] = p.dk + (((int64_t)b * p.S + pos) * p.Hkv + g) * D + lc;
-      dvr[i] = p.dv + (((int64_t)b * p.S + pos) * p.Hkv + g) * D + lc;
+    for (int k = 0; k < 8; ++k) {
+      const int rg = 2 * half + (k >> 2), i = k & 3;
+      const int64_t off = (8 * rg + i) * rstride;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
-        xk[i][db] = dkr[i][db * 32];
-        xv[i][db] = dvr[i][db * 32];
+        xk[k][db] = dk0[off + db * 32];
+        xv[k][db] = dv0[off + db * 32];
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int k = 0; k < 8; ++k) {
+      const int rg = 2 * half + (k >> 2), i = k & 3;
+      const int64_t off = (8 * rg + i) * rstride;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
-        dkr[i][db * 32] = xk[i][db] + p.scale * dk[db][4 * rg + i];
-        dvr[i][db * 32] = xv[i][db] + dv[db][4 * rg + i];
+        dk0[off + db * 32] = xk[k][db] + p.scale * dk[db][4 * rg + i];
+        dv0[off + db * 32] = xv[k][db] + dv[db][4 * rg + i];
       }
+    }
   }
 }
 
@@ -701,24 +704,27 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, char* sA, char* sB, 
   if (!active) return;
   // dQ accumulator: lane holds head_dim column db*32 + lc of queries 8(r/4)+4hl+r%4.  Each
   // 32-rank group lies in one kept block: one lookup per group (see the dK/dV tile).
+  const int64_t rstride = (int64_t)p.Hq * D;                      // elements per token row
 #pragma unroll
   for (int qb = 0; qb < NB; ++qb) {
     const int qpos0 = kt.pos_u(qw0 + 32 * qb);
+    float* const dq0 = p.dq + (((int64_t)b * p.S + qpos0 + 4 * hl) * p.Hq + h) * D + lc;
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      float* dqr[4];
-      float x[4][C::NDB];
+    for (int half = 0; half < 2; ++half) {
+      float x[8][C::NDB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = qpos0 + 8 * rg + 4 * hl + i;
-        dqr[i] = p.dq + (((int64_t)b * p.S + pos) * p.Hq + h) * D + lc;
+      for (int k = 0; k < 8; ++k) {
+        const int64_t off = (8 * (2 * half + (k >> 2)) + (k & 3)) * rstride;
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) x[i][db] = dqr[i][db * 32];
+        for (int db = 0; db < C::NDB; ++db) x[k][db] = dq0[off + db * 32];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int k = 0; k < 8; ++k) {
+        const int rg = 2 * half + (k >> 2), i = k & 3;
+        const int64_t off = (8 * rg + i) * rstride;
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) dqr[i][db * 32] = x[i][db] + p.scale * acc[qb][db][4 * rg + i];
+        for (int db = 0; db < C::NDB; ++db) dq0[off + db * 32] = x[k][db] + p.scale * acc[qb][db][4 * rg + i];
+      }
     }
   }
 }
