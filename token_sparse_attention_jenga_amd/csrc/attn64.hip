@@ -192,16 +192,21 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
       const bool grow = mx > m_run[qb] + kLazyRescale;
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
         const float m_new = fmaxf(m_run[qb], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        float dm = m_run[qb] - m_new;
+        // keep the rescale factor's exponential inside the branch: left alone, the compiler
+        // computes it on every step, one quarter-rate instruction per step for nothing
+        asm volatile("" : "+v"(dm));
+        const float alpha = __builtin_amdgcn_exp2f(dm);
         l_run[qb] *= alpha;
         m_run[qb] = m_new;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) o[qb][db] *= alpha;
       }
       const float m = m_run[qb];
-      float rs = 0.f;
+      st[qb][0] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qb][0], c2, -m));
+      float rs = st[qb][0];                               // (no addition of 0 to start)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 1; r < 16; ++r) {
         const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qb][r], c2, -m));
         st[qb][r] = e;
         rs += e;
