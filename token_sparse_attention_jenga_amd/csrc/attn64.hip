@@ -184,10 +184,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
         for (int r = 0; r < 16; ++r)
           if (8 * (r >> 2) + (r & 3) > lim) st[qb][r] = -INFINITY;
       }
-      float mx = st[qb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[qb][r]);
-      mx = half_pair_max(mx) * c2;               // row max in the log2 domain
+      const float mx = half_pair_max(max16(st[qb])) * c2;  // row max in the log2 domain
       // lazy rescale: move the reference max only when it grows by kLazyRescale or more
       const bool grow = mx > m_run[qb] + kLazyRescale;
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {

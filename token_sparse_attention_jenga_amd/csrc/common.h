@@ -111,9 +111,27 @@ __device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 // Combine lane l with lane l ^ 32 through the cross-half lane swap (a VALU operation, no LDS
 // round trip): the swap of x with itself returns (x[l], x[l + 32]) in lanes l < 32 and
 // (x[l - 32], x[l]) in lanes l >= 32, so both lanes of a pair see the same two values.
+// Maximum of three floats in one v_max3_f32.  Written out because fmaxf makes the compiler
+// first quiet each operand that might be a signalling NaN (one v_max_f32 x, x per operand that
+// does not come from an earlier max), which here costs almost as much as the maximum itself;
+// the operands are scores, never NaN.
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Maximum of the 16 values of a 32x32 accumulator block held by one lane: a tree of v_max3.
+__device__ inline float max16(const f32x16& v) {
+  const float a = max3f(v[0], v[1], v[2]), b = max3f(v[3], v[4], v[5]), c = max3f(v[6], v[7], v[8]);
+  const float d = max3f(v[9], v[10], v[11]), e = max3f(v[12], v[13], v[14]);
+  const float f = max3f(a, b, c), g = max3f(d, e, v[15]);
+  return max3f(f, g, g);
+}
+
 __device__ inline float half_pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
 }
 __device__ inline float half_pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

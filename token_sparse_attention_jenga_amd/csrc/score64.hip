@@ -73,10 +73,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
       for (int r = 0; r < 16; ++r)
         if (kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) > qi) st[r] = -INFINITY;
     }
-    float mx = st[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
-    mx = half_pair_max(mx) * c2;
+    const float mx = half_pair_max(max16(st)) * c2;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kScoreLazy) != 0) {
       const float m_new = fmaxf(m_run, mx);
       float dm = m_run - m_new;
