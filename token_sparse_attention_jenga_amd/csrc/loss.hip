@@ -13,8 +13,14 @@
 
 namespace jenga {
 
-constexpr int kCeThreads = 256;
-constexpr int kCeMaxPerThread = 128;                      // vocab up to 32768
+// One workgroup of 1024 threads per row; thread t holds the float4 groups t, t + 1024, ... of
+// the row (vocab is a multiple of 128, so a group is wholly inside or past the row).  With 32
+// values per thread a wave issues its 8 loads at once and several workgroups share a compute
+// unit; a 256-thread workgroup holding 128 values per thread ran one wave per SIMD and waited
+// out two memory round trips per row.  (Launch bounds: at least 8 waves per SIMD, i.e. two
+// workgroups per compute unit, which keeps a thread within 64 registers.)
+constexpr int kCeThreads = 1024;
+constexpr int kCeGroups = 8;                              // float4 groups per thread: vocab <= 32768
 
 __device__ inline float block_reduce(float v, float* red, bool is_max) {
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -32,31 +38,41 @@ __device__ inline float block_reduce(float v, float* red, bool is_max) {
   return r;
 }
 
-__global__ __launch_bounds__(kCeThreads) void k_ce_rows(CeParams p) {
+__global__ __launch_bounds__(kCeThreads, 8) void k_ce_rows(CeParams p) {
   __shared__ float red[kCeThreads / 64];
   const int row = blockIdx.x, tid = threadIdx.x;
   const float* x = p.logits + (int64_t)row * p.V;
   bf16* g = (bf16*)p.dlogits + (int64_t)row * p.V;
-  float v[kCeMaxPerThread];
+  f32x4 v[kCeGroups];
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kCeMaxPerThread; ++i) {
-    const int c = i * kCeThreads + tid;
-    v[i] = c < p.V ? x[c] : -INFINITY;
-    mx = fmaxf(mx, v[i]);
+  for (int i = 0; i < kCeGroups; ++i) {
+    const int c = 4 * (i * kCeThreads + tid);
+    v[i] = c < p.V ? *(const f32x4*)(x + c) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    mx = fmaxf(mx, fmaxf(fmaxf(v[i][0], v[i][1]), fmaxf(v[i][2], v[i][3])));
   }
   mx = block_reduce(mx, red, true);
   float se = 0.f;
 #pragma unroll
-  for (int i = 0; i < kCeMaxPerThread; ++i) se += __expf(v[i] - mx);
+  for (int i = 0; i < kCeGroups; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) se += __expf(v[i][e] - mx);
   se = block_reduce(se, red, false);
   const float lse = mx + __logf(se);
   const int t = p.targets[row];
   if (tid == 0) p.row_loss[row] = lse - x[t];
 #pragma unroll
-  for (int i = 0; i < kCeMaxPerThread; ++i) {
-    const int c = i * kCeThreads + tid;
-    if (c < p.V) g[c] = (bf16)((__expf(v[i] - lse) - (c == t ? 1.f : 0.f)) * p.grad_scale);
+  for (int i = 0; i < kCeGroups; ++i) {
+    const int c = 4 * (i * kCeThreads + tid);
+    if (c < p.V) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = (__expf(v[i][e] - lse) - (c + e == t ? 1.f : 0.f)) * p.grad_scale;
+      u32x2 w;
+      w[0] = pack_bf16x2(y[0], y[1]);
+      w[1] = pack_bf16x2(y[2], y[3]);
+      *(u32x2*)(g + c) = w;
+    }
   }
 }
 
