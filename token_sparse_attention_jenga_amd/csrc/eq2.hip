@@ -168,8 +168,20 @@ __global__ __launch_bounds__(256, 2) void k_eq2_tiles(Eq2Params p) {
 __global__ __launch_bounds__(256) void k_eq2_reduce(Eq2Params p) {
   const int b = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
   if (n >= p.nkb) return;
+  const float* col = p.tilemax + (int64_t)b * p.nkb * p.nkb + n;
+  // the sum runs over m in ascending order; the reads of 16 terms are issued before they are
+  // added, so the loop waits once per 16 terms instead of once per term
+  constexpr int U = 16;
   double s = 0.0;
-  for (int m = n; m < p.nkb; ++m) s += (double)p.tilemax[((int64_t)b * p.nkb + m) * p.nkb + n];
+  int m = n;
+  for (; m + U <= p.nkb; m += U) {
+    float t[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) t[i] = col[(int64_t)(m + i) * p.nkb];
+#pragma unroll
+    for (int i = 0; i < U; ++i) s += (double)t[i];
+  }
+  for (; m < p.nkb; ++m) s += (double)col[(int64_t)m * p.nkb];
   p.scores[(int64_t)b * p.nkb + n] = (float)s;
 }
 

@@ -223,10 +223,26 @@ __global__ void k_score_reduce(ScoreParams p) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= nkb) return;
   const int gpb = p.block / 32, ng = p.S / 32;
+  const double* base = p.mass32 + (int64_t)b * p.Hq * ng + n * gpb;
+  // terms k = h * gpb + c summed in ascending k; the reads of 16 terms are issued before they
+  // are added, so the loop waits once per 16 terms instead of once per term
+  constexpr int U = 16;
+  const int K = p.Hq * gpb;
   double s = 0.0;
-  for (int h = 0; h < p.Hq; ++h) {
-    const double* row = p.mass32 + ((int64_t)b * p.Hq + h) * ng + n * gpb;
-    for (int c = 0; c < gpb; ++c) s += row[c];
+  int k = 0;
+  for (; k + U <= K; k += U) {
+    double t[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int h = (k + i) / gpb, c = k + i - h * gpb;
+      t[i] = base[(int64_t)h * ng + c];
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) s += t[i];
+  }
+  for (; k < K; ++k) {
+    const int h = k / gpb, c = k - h * gpb;
+    s += base[(int64_t)h * ng + c];
   }
   p.scores[(int64_t)b * nkb + n] = (float)(s / p.Hq);
 }
