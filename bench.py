@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 
 BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 bf16 flop/clk/CU x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
-KERNELS = ("k_slse64", "k_smass64", "k_eq2_tiles", "k_eq2_reduce", "k_select", "k_pack_tp",
+KERNELS = ("k_slse64", "k_sblock_mass", "k_eq2_tiles", "k_eq2_reduce", "k_select", "k_pack_tp",
            "k_fwd64", "k_prep64", "k_bwd64", "k_proj_gather", "k_proj_scatter",
            "k_proj_logits", "k_ce_rows", "k_proj_dh", "k_mlp_act_gated", "k_mlp_block",
            "k_proj_gather_scatter")

@@ -87,9 +87,12 @@ size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks
  * For every batch row and key block n:
  *   block_scores[b][n] = (1/Hq) * sum_h sum_{j in block n} sum_{i > j} P^h_ij,
  * where P^h is the causal softmax of scale * q_i . k_j over all S tokens of head h (KV head
- * h / (Hq/Hkv)); the self term i = j is excluded as in Eq. 1.  Computed in two streamed
- * passes (row log-sum-exp, then received mass per key) without storing any S x S matrix.
- * The result is deterministic: per-key sums are fp64 and reduced in a fixed order.
+ * h / (Hq/Hkv)); the self term i = j is excluded as in Eq. 1.  No S x S matrix is stored.
+ * bf16: one streamed pass over the causal scores yields each row's log-sum-exp and, per query
+ * and key block, the log2 of the block's partial sum (S^2 / (2 block) floats per head in the
+ * workspace); a second, memory-bound pass turns these into the mass per key block.  fp32: two
+ * streamed passes (row log-sum-exp, then received mass per key).  The result is
+ * deterministic: sums are fp64 and reduced in a fixed order.
  *
  *   q            [B][S][Hq][D] (dtype, strided per q_stride)
  *   k            [B][S][Hkv][D] (dtype, strided per k_stride)
@@ -336,7 +339,7 @@ int jenga_lm_head_ce_segmented(const jenga_loss_problem* p, const void* h, const
  * jenga_timing_enable(1) discards earlier records and, from then on, brackets every kernel
  * launched by the entry points above with two HIP events recorded on that call's stream;
  * jenga_timing_enable(0) stops recording (the records stay readable).  Kernel names:
- * k_slse64, k_smass64 (bf16 scoring), k_eq2_tiles, k_eq2_reduce (Eq. 2 scoring), k_select,
+ * k_slse64, k_sblock_mass (bf16 scoring), k_eq2_tiles, k_eq2_reduce (Eq. 2 scoring), k_select,
  * k_pack_tp, k_fwd64, k_prep64, k_bwd64 (bf16 attention; k_bwd64 is one launch per backward
  * segment, with the dK/dV and dQ tiles), k_proj_gather, k_proj_scatter, k_proj_gather_scatter,
  * k_mlp_act_gated, k_mlp_act_relu, k_mlp_block (MLP elimination), k_proj_logits, k_ce_rows,

@@ -93,10 +93,19 @@ size_t score_eq2_ws_bytes(const jenga_problem* p) {
   return align_up((size_t)p->batch * nkb * nkb * sizeof(float));
 }
 
+// per (batch, head): the causal triangle of key-block partial log2-sums (bf16 path)
+size_t score_tri_elems(const jenga_problem* p) {
+  const size_t nkb = p->seq_len / p->block;
+  return nkb * p->seq_len - (size_t)p->block * nkb * (nkb - 1) / 2;
+}
+
 size_t score_ws_bytes(const jenga_problem* p) {
   const size_t lse = (size_t)p->batch * p->n_heads_q * p->seq_len * sizeof(float);
   const size_t mass = (size_t)p->batch * p->n_heads_q * (p->seq_len / 32) * sizeof(double);
-  return align_up(lse) + align_up(mass);
+  const size_t tri = p->dtype == JENGA_DTYPE_BF16
+                         ? (size_t)p->batch * p->n_heads_q * score_tri_elems(p) * sizeof(float)
+                         : 0;
+  return align_up(lse) + align_up(mass) + align_up(tri);
 }
 
 int check_proj(const jenga_proj_problem* p, const void* in, const void* w, const int32_t* kept,
@@ -261,6 +270,9 @@ int jenga_score_blocks(const jenga_problem* p, const void* q, const void* k, flo
   sp.lse2 = (float*)workspace;
   sp.mass32 = (double*)((char*)workspace +
                         align_up((size_t)p->batch * p->n_heads_q * p->seq_len * sizeof(float)));
+  sp.lpart = (float*)((char*)sp.mass32 +
+                      align_up((size_t)p->batch * p->n_heads_q * (p->seq_len / 32) * sizeof(double)));
+  sp.mass_gpb = 0;
   sp.scores = block_scores;
   if (jenga::launch_score(sp, p->dtype, p->head_dim, (hipStream_t)stream) != hipSuccess)
     return JENGA_ERR_LAUNCH;

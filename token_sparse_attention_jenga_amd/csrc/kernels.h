@@ -13,7 +13,10 @@ struct ScoreParams {
   int B, S, Hq, Hkv, block;
   float scale_log2;   // softmax scale * log2(e)
   float* lse2;        // workspace [B][Hq][S]: log2-domain row normaliser
-  double* mass32;     // workspace [B][Hq][S/32]: received mass per 32-key group
+  double* mass32;     // workspace [B][Hq][S/32]: received mass per group of keys
+  float* lpart;       // workspace, bf16 path: per (batch, head) the causal triangle of partial
+                      // log2-sums, row n (key block n) holding queries n*block .. S-1
+  int mass_gpb;       // mass32 groups per key block (set by launch_score)
   float* scores;      // [B][S/block]
 };
 

@@ -222,7 +222,7 @@ __global__ void k_score_reduce(ScoreParams p) {
   const int nkb = p.S / p.block;
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= nkb) return;
-  const int gpb = p.block / 32, ng = p.S / 32;
+  const int gpb = p.mass_gpb, ng = nkb * gpb;
   const double* base = p.mass32 + (int64_t)b * p.Hq * ng + n * gpb;
   // terms k = h * gpb + c summed in ascending k; the reads of 16 terms are issued before they
   // are added, so the loop waits once per 16 terms instead of once per term
@@ -260,14 +260,17 @@ static hipError_t launch_score_t(const ScoreParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_score(const ScoreParams& p, int dtype, int D, hipStream_t st) {
-  if (dtype == 1) {                      // bf16: async-staged kernels of score64.hip
+hipError_t launch_score(const ScoreParams& p0, int dtype, int D, hipStream_t st) {
+  ScoreParams p = p0;
+  if (dtype == 1) {                      // bf16: one pass of score64.hip, mass per key block
+    p.mass_gpb = 1;
     hipError_t e = launch_score64(p, D, st);
     if (e != hipSuccess) return e;
     const int nkb = p.S / p.block;
     k_score_reduce<<<dim3((nkb + 255) / 256, p.B), 256, 0, st>>>(p);
     return hipGetLastError();
   }
+  p.mass_gpb = p.block / 32;             // fp32: mass per 32-key group
   return launch_score_t<float, 64>(p, st);    // fp32 operands: head_dim 64 only
 }
 

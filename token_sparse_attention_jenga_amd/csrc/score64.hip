@@ -4,12 +4,17 @@
 // receives from all other tokens; §4.2.2 Eq. 2: averaged over heads; §4.2.3: aggregated per key
 // block over the query blocks).  The interaction is the causal softmax probability.
 //
-//   k_slse64   query-major, 32 queries per wave: lse2_i = log2 sum_{j<=i} 2^(c q_i.k_j);
-//              S^T = K Q^T per 32-key step, running max (lazily moved) and an fp64 running sum.
-//   k_smass64  key-major, 32 keys per wave (K in registers): per 32-query step
-//              S = Q K^T, p = 2^(c S - lse2_i) for i > j, per-key fp32 partial sums added into
-//              fp64; finally a fixed-order fp64 reduction to 32-key groups.
-// Both are VALU-bound (one exp per score); the MFMA work is half of it or less.
+// The received mass of key block n sums p_ij = 2^(c q_i.k_j - lse2_i) over its keys j and the
+// queries i > j.  Grouped by query, that is sum_i 2^(L_in - lse2_i) with the partial log2-sum
+// L_in = log2 sum_{j in n, j < i} 2^(c q_i.k_j): the exponentials that make lse2_i also make
+// every L_in, so one pass over the causal scores suffices.
+//
+//   k_slse64       query-major, 32 queries per wave, S^T = K Q^T per 32-key step, running max
+//                  (lazily moved): lse2_i with an fp64 running sum, and L_in per key block
+//                  (fp32 block sum, stored as a log2 when the block ends).  VALU-bound: one
+//                  exponential per score; the MFMA work is half of it or less.
+//   k_sblock_mass  per (batch, head, key block): sum_i 2^(L_in - lse2_i) over the block's row of
+//                  the triangle, fp32 groups of 4 added into fp64, fixed order.  HBM-bound.
 #include "common.h"
 #include "kernels.h"
 #include "tiles64.h"
@@ -58,6 +63,21 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
   const float c2 = p.scale_log2;
   float m_run = -INFINITY;
   double l_run = 0.0;
+  // key-block partial sum (relative to m_run) of the scores of keys before the query
+  float bsum = 0.f;
+  const int tpb = p.block / 32;                          // key steps per block
+  int in_blk = 0, blk = 0;                               // wave-uniform block position
+  // this (batch, head)'s triangle: row n at n*S - block*n(n-1)/2, queries n*block .. S-1
+  const int nkb = p.S / p.block;
+  float* const lp = p.lpart + ((int64_t)b * p.Hq + h) *
+                                  ((int64_t)nkb * p.S - (int64_t)p.block * nkb * (nkb - 1) / 2);
+  int row_off = 0;                                       // row blk's offset minus blk*block
+  // a finished block's value is stored at the start of the next step, after that step's wait
+  // and before its tile loads are issued: stored right away, it would sit behind those loads
+  // and the next step's wait would have to take it along
+  bool pend = false;
+  float pend_v = 0.f;
+  int pend_i = 0;
 
   const rsrc_t rk = make_rsrc_u(kbase);
   auto issue = [&](int t, char* buf) { kplan.issue(buf, rk, (uint32_t)(32 * t * kstride)); };
@@ -68,7 +88,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) st = Mfma<bf16>::mma(ldo(Kl, rp.nat[s]), qf[s], st);
     SCHED_READS_AHEAD(C::NS, 1, 1, 0);
-    if (kr0 + 31 > qw0) {                                // diagonal step: causal mask
+    const bool diag = kr0 == qw0;                        // the wave's last step
+    if (diag) {                                          // causal mask
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) > qi) st[r] = -INFINITY;
@@ -80,14 +101,43 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
       // keep the rescale factor's exponential inside the branch: left alone, the compiler
       // computes it on every step, one quarter-rate instruction per step for nothing
       asm volatile("" : "+v"(dm));
-      l_run *= (double)__builtin_amdgcn_exp2f(dm);
+      const float f = __builtin_amdgcn_exp2f(dm);
+      l_run *= (double)f;
+      bsum *= f;
       m_run = m_new;
     }
-    // (the sum starts from its first term: starting from 0 costs an addition per step)
-    float rs = __builtin_amdgcn_exp2f(__builtin_fmaf(st[0], c2, -m_run));
+    if (!diag) {
+      // (the sum starts from its first term: starting from 0 costs an addition per step)
+      float rs = __builtin_amdgcn_exp2f(__builtin_fmaf(st[0], c2, -m_run));
 #pragma unroll
-    for (int r = 1; r < 16; ++r) rs += __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c2, -m_run));
-    l_run += (double)rs;
+      for (int r = 1; r < 16; ++r) rs += __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c2, -m_run));
+      l_run += (double)rs;
+      bsum += rs;
+    } else {                                             // the mass leaves out the key i = j
+      float rs = 0.f, rm = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c2, -m_run));
+        rs += e;
+        rm += (kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) < qi) ? e : 0.f;
+      }
+      l_run += (double)rs;
+      bsum += rm;
+    }
+    if (++in_blk == tpb || diag) {                       // block ends here for these queries
+      const float tot = half_pair_sum(bsum);             // lanes l, l^32: the two key halves
+      pend_v = m_run + __builtin_amdgcn_logf(tot);       // log2; of 0, -inf: no key before i
+      pend_i = row_off + qi;
+      pend = true;
+      bsum = 0.f;
+      in_blk = 0;
+      row_off += p.S - p.block * (blk + 1);              // row blk + 1, minus (blk + 1)*block
+      ++blk;
+    }
+  };
+  auto flush = [&]() {
+    if (pend && hl == 0) lp[pend_i] = pend_v;
+    pend = false;
   };
   auto stage = [&](int t, const char* cur, char* nxt) {
     // every step issues one tile (past the end, a reload of the last one that nobody reads), so
@@ -95,122 +145,64 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
     if (!DC::EXACT) wait_all_mem();
     else wait_vm<PER>();
     stage_barrier();
+    flush();
     issue(min(t + 2, nsteps - 1), nxt);
     compute(t, cur);
   };
   issue(0, sA);
   issue(min(1, nsteps - 1), sB);
   ring3_loop(nsteps, sA, sB, sC, stage);
+  flush();
   wait_all_mem();                                        // drain the trailing reloads
   if (!active) return;
   const double lsum = l_run + __shfl_xor(l_run, 32, 64);
   if (hl == 0) p.lse2[((int64_t)b * p.Hq + h) * p.S + qi] = (float)((double)m_run + log2(lsum));
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void k_smass64(ScoreParams p) {
-  using C = T64<D>;
-  using DC = DmaCount<D, NW>;
-  constexpr int LDC = 8 / NW;                      // 16-byte chunks of the 32 lse2 values per wave
-  static_assert(8 % NW == 0, "lse2 chunks must split evenly over the waves");
-  constexpr int PER = DC::NAT_W + 1;
-  constexpr int KG = 32 * NW;
-  constexpr int STAGE = C::NAT32 + 128;
-  __shared__ __attribute__((aligned(1024))) char sA[STAGE];
-  __shared__ __attribute__((aligned(1024))) char sB[STAGE];
-  __shared__ __attribute__((aligned(1024))) char sC[STAGE];
+// Received mass of key block n for one (batch, head): sum over the queries i of the block's
+// triangle row of 2^(L_in - lse2_i).  One workgroup per row; each thread adds groups of four
+// terms (fp32) into an fp64 sum, then a fixed-order reduction over the workgroup.
+constexpr int kMassThreads = 256;
 
-  const Tile3 tl = xcd_tile();
-  const int b = tl.z, h = tl.y;
-  const int g = h / (p.Hq / p.Hkv);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
-  const int k0 = tl.x * KG;
-  const int kw0 = k0 + 32 * w;
-  const bool active = kw0 < p.S;
-  const int kj = kw0 + lc;
-  const int nsteps = (p.S - k0) / 32;              // query steps k0, k0+32, ..., S-32
-
-  bf16x8 kf[C::NS];
-  if (active) {
-    const char* krow = (const char*)((const bf16*)p.k + b * p.ks[0] + (int64_t)kj * p.ks[1] + g * p.ks[2]);
-#pragma unroll
-    for (int s = 0; s < C::NS; ++s) kf[s] = *(const bf16x8*)(krow + (16 * s + 8 * hl) * 2);
-  }
-  // retire the register operand loads now: a load still pending when the staged loop starts
-  // would make the compiler wait for all vector memory, prefetched tiles included, at its first
-  // use in every iteration
-  wait_all_mem();
-  const char* qbase = (const char*)((const bf16*)p.q + b * p.qs[0] + h * p.qs[2]);
-  const int64_t qstride = p.qs[1] * 2;
-  const float* lrow = p.lse2 + ((int64_t)b * p.Hq + h) * p.S;
-  NatPlan<D, NW> qplan;
-  qplan.init(qstride);
-  ReadPlan<D> rp;
-  rp.init();
-  const float c2 = p.scale_log2;
+__global__ __launch_bounds__(kMassThreads) void k_sblock_mass(ScoreParams p) {
+  const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nkb = p.S / p.block;
+  const int64_t tri = (int64_t)nkb * p.S - (int64_t)p.block * nkb * (nkb - 1) / 2;
+  const int64_t row = (int64_t)n * p.S - (int64_t)p.block * n * (n - 1) / 2;
+  const float* lrow = p.lpart + ((int64_t)b * p.Hq + h) * tri + row;
+  const float* lse = p.lse2 + ((int64_t)b * p.Hq + h) * p.S + n * p.block;
+  const int len = p.S - n * p.block;                     // a multiple of 64
   double acc = 0.0;
-
-  const rsrc_t rq = make_rsrc_u(qbase), rl = make_rsrc_u(lrow);
-  const uint32_t lvoff = 16u * (LDC * w + l);
-  auto issue = [&](int t, char* buf) {
-    const int q0 = k0 + 32 * t;
-    qplan.issue(buf, rq, (uint32_t)(q0 * qstride));
-    if (l < LDC) dma16b(rl, lvoff, (uint32_t)q0 * 4u, buf + C::NAT32 + 16 * LDC * w);
-  };
-  auto compute = [&](int t, const char* buf) {
-    const int q0 = k0 + 32 * t;
-    if (!active || q0 + 31 <= kw0) return;         // no query of the step follows a key
-    f32x16 st = zero16();
+  constexpr int U = 4;                                   // groups whose loads are issued together
+  int i = 4 * threadIdx.x;
+  for (; i + 4 * kMassThreads * (U - 1) < len; i += 4 * kMassThreads * U) {
+    f32x4 a[U], c[U];
 #pragma unroll
-    for (int s = 0; s < C::NS; ++s) st = Mfma<bf16>::mma(ldo(buf, rp.nat[s]), kf[s], st);
-    SCHED_READS_AHEAD(C::NS, 1, 1, 0);
-    const float* ls = (const float*)(buf + C::NAT32);
-    float colsum = 0.f;
-    if (q0 <= kw0 + 31) {                          // diagonal step: only queries after the key
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4 lq = *(const f32x4*)(ls + 8 * rg + 4 * hl);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[4 * rg + i], c2, -lq[i]));
-          colsum += (q0 + 8 * rg + 4 * hl + i > kj) ? e : 0.f;
-        }
-      }
-    } else {
-      // (the sum starts from its first term: starting from 0 costs an addition per step)
-      const f32x4 lq0 = *(const f32x4*)(ls + 4 * hl);
-      colsum = __builtin_amdgcn_exp2f(__builtin_fmaf(st[0], c2, -lq0[0]));
-#pragma unroll
-      for (int i = 1; i < 4; ++i) colsum += __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], c2, -lq0[i]));
-#pragma unroll
-      for (int rg = 1; rg < 4; ++rg) {
-        const f32x4 lq = *(const f32x4*)(ls + 8 * rg + 4 * hl);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) colsum += __builtin_amdgcn_exp2f(__builtin_fmaf(st[4 * rg + i], c2, -lq[i]));
-      }
+    for (int u = 0; u < U; ++u) {
+      a[u] = *(const f32x4*)(lrow + i + 4 * kMassThreads * u);
+      c[u] = *(const f32x4*)(lse + i + 4 * kMassThreads * u);
     }
-    acc += (double)colsum;
-  };
-  auto stage = [&](int t, const char* cur, char* nxt) {
-    // every step issues one tile (past the end, a reload of the last one that nobody reads), so
-    // exactly one tile's loads may still be in flight when tile t is needed
-    if (!DC::EXACT) wait_all_mem();
-    else wait_vm<PER>();
-    stage_barrier();
-    issue(min(t + 2, nsteps - 1), nxt);
-    compute(t, cur);
-  };
-  if (nsteps > 0) {
-    issue(0, sA);
-    issue(min(1, nsteps - 1), sB);
-    ring3_loop(nsteps, sA, sB, sC, stage);
-  }
-  wait_all_mem();                                        // drain the trailing reloads
-  // lanes l and l^32 hold the same key; then a fixed butterfly over the wave's 32 keys
-  acc += __shfl_xor(acc, 32, 64);
 #pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (active && l == 0) p.mass32[((int64_t)b * p.Hq + h) * (p.S / 32) + kw0 / 32] = acc;
+    for (int u = 0; u < U; ++u)
+      acc += (double)((__builtin_amdgcn_exp2f(a[u][0] - c[u][0]) + __builtin_amdgcn_exp2f(a[u][1] - c[u][1])) +
+                      (__builtin_amdgcn_exp2f(a[u][2] - c[u][2]) + __builtin_amdgcn_exp2f(a[u][3] - c[u][3])));
+  }
+  for (; i < len; i += 4 * kMassThreads) {
+    const f32x4 a = *(const f32x4*)(lrow + i), c = *(const f32x4*)(lse + i);
+    acc += (double)((__builtin_amdgcn_exp2f(a[0] - c[0]) + __builtin_amdgcn_exp2f(a[1] - c[1])) +
+                    (__builtin_amdgcn_exp2f(a[2] - c[2]) + __builtin_amdgcn_exp2f(a[3] - c[3])));
+  }
+  __shared__ double part[kMassThreads / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = part[0];
+#pragma unroll
+    for (int w = 1; w < kMassThreads / 64; ++w) t += part[w];
+    p.mass32[((int64_t)b * p.Hq + h) * nkb + n] = t;
+  }
 }
 
 constexpr int SCORE_NW = 4;
@@ -225,8 +217,8 @@ static hipError_t launch_score64_t(const ScoreParams& p, hipStream_t st) {
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  TimedLaunch tl("k_smass64", st);
-  k_smass64<D, SCORE_NW><<<dim3((p.S + RG - 1) / RG, p.Hq, p.B), 64 * SCORE_NW, 0, st>>>(p);
+  TimedLaunch tl("k_sblock_mass", st);
+  k_sblock_mass<<<dim3(p.S / p.block, p.Hq, p.B), kMassThreads, 0, st>>>(p);
   return hipGetLastError();
 }
 
