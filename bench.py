@@ -299,7 +299,7 @@ def main():
     bwd_flop = 10.0 * D * Hq * pairs
     attn_ms = phase["fwd"] + phase["bwd"]
     tflops = (fwd_flop + bwd_flop) / (attn_ms * 1e-3) / 1e12
-    score_flop = 2 * 2.0 * D * Hq * B * L * S * (S + 1) / 2
+    score_flop = 2.0 * D * Hq * B * L * S * (S + 1) / 2       # one q.k per causal pair and head
 
     # dominant attention kernel: k_bwd64 (one launch per backward segment, running the dK/dV
     # and dQ tiles of the segment), timed by the library's own HIP events on the stream it runs
@@ -485,12 +485,13 @@ def main():
            "fwd_workspace_mib": round(layers[0]["ws_f"].numel() / 2**20, 2),
            "bwd_workspace_mib": round(layers[0]["ws_b"].numel() / 2**20, 2)}
 
-    # Per-step evidence beside the metric: the exponentials per second of the two scoring passes
-    # (one exp per causal pair per query head in each pass), and the backward prologue's
+    # Per-step evidence beside the metric: the exponentials per second of scoring (one exp per
+    # causal pair per query head, in the row pass; the block-mass pass adds one per query and
+    # key block, not counted), and the backward prologue's
     # bytes per second (per kept query row and head: dOut row fp32 and o_saved row in, lse in;
     # D, lse2, the dOut row in operand dtype and its transposed copy out).
     es = 2 if cfg.dtype == "bf16" else 4
-    score_exps = 2.0 * Hq * B * L * S * (S + 1) / 2
+    score_exps = 1.0 * Hq * B * L * S * (S + 1) / 2
     step_evidence = {"score_exp_per_s": round(score_exps / (phase["score"] * 1e-3), 1)}
     n_prep, t_prep = kern_ms.get("k_prep64", (0, 0.0))
     if n_prep:
