@@ -78,19 +78,25 @@ def test_select_batched(J):
 # ----------------------------------------------------------------------------------------
 
 SCORE_CASES = [
-    # B, S, Hq, Hkv, D, block, dtype
-    (1, 1024, 8, 8, 64, 64, "f32"),
-    (1, 512, 4, 4, 128, 64, "bf16"),
-    (2, 384, 4, 2, 128, 128, "bf16"),
-    (1, 448, 2, 1, 64, 64, "bf16"),
+    # B, S, Hq, Hkv, D, block, dtype, input std (None: 1 for f32, 1/sqrt(D) for bf16)
+    (1, 1024, 8, 8, 64, 64, "f32", None),
+    (1, 512, 4, 4, 128, 64, "bf16", None),
+    (2, 384, 4, 2, 128, 128, "bf16", None),
+    (1, 448, 2, 1, 64, 64, "bf16", None),
+    # a block of three 32-key steps, and the largest block (32 steps)
+    (1, 576, 2, 2, 128, 192, "bf16", None),
+    (1, 2048, 2, 1, 128, 1024, "bf16", None),
+    # logits of standard deviation about 8 in log2 units: the running maximum of a query row
+    # moves inside key blocks, so the block partial sums are rescaled on the way
+    (1, 1024, 2, 2, 128, 64, "bf16", 2.0),
 ]
 
 
-@pytest.mark.parametrize("B,S,Hq,Hkv,D,block,dtype", SCORE_CASES)
-def test_scores(J, B, S, Hq, Hkv, D, block, dtype):
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,block,dtype,std", SCORE_CASES)
+def test_scores(J, B, S, Hq, Hkv, D, block, dtype, std):
     import torch
-    q, k, _, _, _ = random_inputs(B, S, Hq, Hkv, D, dtype, seed=S + Hq)
-    say(f"scores B{B} S{S} Hq{Hq} Hkv{Hkv} D{D} block{block} {dtype}")
+    q, k, _, _, _ = random_inputs(B, S, Hq, Hkv, D, dtype, seed=S + Hq, std=std)
+    say(f"scores B{B} S{S} Hq{Hq} Hkv{Hkv} D{D} block{block} {dtype} std{std}")
     got = J.score_blocks(to_device(q, dtype), to_device(k, dtype), block)
     torch.cuda.synchronize()
     ref = oracle.block_scores(q, k, block)
