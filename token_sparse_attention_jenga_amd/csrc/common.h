@@ -155,4 +155,22 @@ __device__ inline Tile3 xcd_tile() {
   return {L % nx, (L / nx) % ny, L / (nx * ny)};
 }
 
+// The same XCD-contiguous ranges for a GEMM grid (x = row tiles, y = column tiles), with the
+// tiles of a range visited in groups of GM row tiles: within a group the row tile runs fastest,
+// so the workgroups an XCD runs side by side cover GM row panels and a few column panels, and
+// each panel's reduction chunks serve several of them from the L2 (row tile fastest over all
+// row tiles would have them share column panels only).
+template <int GM>
+__device__ inline Tile3 xcd_tile_grouped() {
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int nwg = nx * ny * (int)gridDim.z;
+  const int lin = (int)blockIdx.x + nx * ((int)blockIdx.y + ny * (int)blockIdx.z);
+  const int q = nwg >> 3, r = nwg & 7, xcd = lin & 7, slot = lin >> 3;
+  const int L = xcd * q + min(xcd, r) + slot;
+  const int per = nx * ny, z = L / per, Lr = L - z * per;
+  const int grp = Lr / (GM * ny), first = grp * GM, g = min(nx - first, GM);
+  const int in = Lr - grp * GM * ny;
+  return {first + in % g, in / g, z};
+}
+
 }  // namespace jenga
