@@ -136,6 +136,24 @@ def test_workspace_scales_with_segments_and_kept_blocks(J):
     assert J.workspace_bytes(_problem(J), J.JENGA_OP_FWD, 8) == 0       # fp32 path needs none
 
 
+def test_score_workspace(J):
+    # lse2 rows (fp32) and mass slots (fp64, one per 32 keys), each rounded to 256 bytes; the
+    # bf16 path adds, per (batch, head), the causal triangle of key-block partial log2-sums:
+    # row n holds the queries n*block .. S-1, S*nKB - block*nKB*(nKB-1)/2 floats in all
+    up = lambda x: (x + 255) // 256 * 256
+    for B, S, Hq, block in ((1, 32768, 32, 128), (2, 4096, 8, 64), (1, 576, 2, 192)):
+        nkb = S // block
+        tri = S * nkb - block * nkb * (nkb - 1) // 2
+        base = up(B * Hq * S * 4) + up(B * Hq * (S // 32) * 8)
+        p16 = _problem(J, B=B, S=S, Hq=Hq, Hkv=Hq, D=128, block=block, dtype=1)
+        assert J.workspace_bytes(p16, J.JENGA_OP_SCORE) == base + up(B * Hq * tri * 4)
+        p32 = _problem(J, B=B, S=S, Hq=Hq, Hkv=Hq, D=64, block=block, dtype=0)
+        assert J.workspace_bytes(p32, J.JENGA_OP_SCORE) == base
+    # 32K tokens, 32 heads, block 128: 514 MiB of partial sums beside 4.25 MiB of rows and slots
+    c5 = _problem(J, S=32768, Hq=32, Hkv=32, D=128, block=128, dtype=1)
+    assert J.workspace_bytes(c5, J.JENGA_OP_SCORE) == 4 * 2**20 + 2**18 + 32 * 4210688 * 4
+
+
 def test_timing_calls_without_gpu_work(J):
     assert J.lib.jenga_timing_enable(2) == J.JENGA_ERR_INVALID_ARG
     J.timing_enable(True)
