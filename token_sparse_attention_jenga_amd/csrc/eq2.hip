@@ -22,9 +22,10 @@
 namespace jenga {
 
 // Score blocks are visited in super-tiles of kSM query blocks x kSN key blocks, one
-// workgroup per block: the kSM * kSN = 32 workgroups an XCD runs at a time (one per compute
-// unit) then share kSM Q and kSN K blocks per head in that XCD's L2, instead of one Q block
-// and 32 different K blocks.  Super-tile (M, N) holds the blocks m in [kSM M, kSM M + kSM),
+// workgroup per block: the kSM * kSN = 32 consecutive workgroups of an XCD's range run side by
+// side and share kSM Q and kSN K blocks per head in that XCD's L2, instead of one Q block and
+// 32 different K blocks.  (8 x 8 super-tiles, as many as the XCD's 32 compute units hold at two
+// workgroups each, measured no faster.)  Super-tile (M, N) holds the blocks m in [kSM M, kSM M + kSM),
 // n in [kSN N, kSN N + kSN); only super-tiles holding some causal block (m >= n) are
 // launched, N-major, and slots with m < n or past the last block exit at once.
 constexpr int kSM = 4, kSN = 8;
