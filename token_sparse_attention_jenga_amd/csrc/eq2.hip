@@ -105,9 +105,13 @@ __global__ __launch_bounds__(256, 2) void k_eq2_tiles(Eq2Params p) {
   f32x16 acc[SPW], sc[SPW];
 #pragma unroll
   for (int t = 0; t < SPW; ++t) acc[t] = sc[t] = zero16();
-  // sub-tile t of this wave: query sub-block qsb(t), key sub-block ksb(t)
-  auto qsb = [&](int t) { return (w * SPW + t) / SB; };
-  auto ksb = [&](int t) { return (w * SPW + t) % SB; };
+  // sub-tile t of this wave: query sub-block qsb(t), key sub-block ksb(t).  The waves take the
+  // four quadrants of the SB x SB sub-tiles, so a wave's SB/2 query and SB/2 key operand reads
+  // of a k-step serve (SB/2)^2 MFMAs
+  constexpr int HB = SB / 2;
+  static_assert(HB * HB == SPW, "one quadrant of sub-tiles per wave");
+  auto qsb = [&](int t) { return (w >> 1) * HB + t / HB; };
+  auto ksb = [&](int t) { return (w & 1) * HB + t % HB; };
 
   auto compute = [&](int u, const char* buf) {
 #pragma unroll
