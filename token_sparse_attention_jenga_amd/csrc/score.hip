@@ -1,5 +1,7 @@
 // Block-level token informativeness on gfx950: received attention-probability mass per key
-// block, streamed in two passes without ever storing an S x S matrix.
+// block, without ever storing an S x S matrix.  This file holds the fp32-operand path, streamed
+// in two passes, the launcher of both paths and the reduction over heads they share (the bf16
+// path is score64.hip).
 //
 // Jenga (aipaper summary, §4.2.1 Eq. 1: a token's informativeness sums the interaction it
 // receives from every other token, self excluded; §4.2.2 Eq. 2: per-head values are averaged
@@ -10,7 +12,8 @@
 //                          c = scale*log2(e); online max/sum, the running sum in fp64.
 //   pass 2 (k_score_mass): key-major; per key j, M(j) = sum_{i>j} 2^(c q_i.k_j - lse2_i),
 //                          summed per 32-key group in fp64, in a fixed order.
-//   reduce (k_score_reduce): s[b][n] = (1/Hq) sum_h sum_{groups of block n}, fp64 -> fp32.
+//   reduce (k_score_reduce): s[b][n] = (1/Hq) sum_h sum_{groups of block n}, fp64 -> fp32
+//                          (block/32 groups per block here; the bf16 path leaves one).
 #include "common.h"
 #include "kernels.h"
 
