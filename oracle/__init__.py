@@ -11,6 +11,6 @@ from .jenga_oracle import (SELECT_TOPK, SELECT_THRESH_REL, SELECT_THRESH_ABS, at
                            proj_scatter_add, proj_gather_scatter_add, MLP_RELU,
                            MLP_SILU_GATED, mlp_activation, mlp_token_scores,
                            mlp_block_scores, mlp_sparse_forward,
-                           compact_saved, default_scale, keep_count, kv_head_of,
+                           default_scale, keep_count, kv_head_of,
                            received_mass, residual_add, select_blocks, stack_forward,
                            threshold_value, token_positions)
