@@ -205,13 +205,14 @@ def proj_scatter_add(resid, y, w, kept, block: int) -> np.ndarray:
 # ([summary] 4.4.2; [notes] 4.4): cross-entropy of softmax(h W^T) against the next tokens.
 # ----------------------------------------------------------------------------------------
 
-def lm_head_ce(h, w, targets):
+def lm_head_ce(h, w, targets, with_logit_grad: bool = False):
     """Mean cross-entropy over the T rows of h and its gradient with respect to h.
 
     h: [T, d]; w: [V, d] (the head's weight); targets: [T] ints in [0, V).
     logits = h w^T; row_loss_t = logsumexp(logits_t) - logits_t[target_t];
-    loss = mean_t row_loss_t; dh = ((softmax(logits) - onehot(targets)) / T) w.
-    Returns (loss, row_loss [T], dh [T, d]) in float64."""
+    loss = mean_t row_loss_t; dh = g w with the logit gradient g = (softmax(logits) -
+    onehot(targets)) / T.
+    Returns (loss, row_loss [T], dh [T, d]) in float64, and g [T, V] when with_logit_grad."""
     h, w = _f64(h), _f64(w)
     T = h.shape[0]
     logits = h @ w.T
@@ -221,7 +222,10 @@ def lm_head_ce(h, w, targets):
     row_loss = lse - logits[np.arange(T), t]
     g = np.exp(logits - lse[:, None])
     g[np.arange(T), t] -= 1.0
-    dh = (g / T) @ w
+    g /= T
+    dh = g @ w
+    if with_logit_grad:
+        return float(row_loss.mean()), row_loss, dh, g
     return float(row_loss.mean()), row_loss, dh
 
 
@@ -484,18 +488,6 @@ def residual_add(resid, O, kept, block: int) -> np.ndarray:
     return out
 
 
-def compact_saved(O, LSE, kept, block: int):
-    """The saved activations in kept-rank order: o_saved [B,Nk,Hq,D], lse [B,Hq,Nk]."""
-    B = O.shape[0]
-    keptb = _per_batch(kept, B)
-    outs, lses = [], []
-    for b in range(B):
-        pos = token_positions(keptb[b], block)
-        outs.append(O[b, pos])
-        lses.append(LSE[b][:, pos])
-    return outs, lses
-
-
 def attn_bwd_masked(q, k, v, kept, block: int, dout, scale: float = None):
     """Gradients of L = <dout, O> under the explicit mask.
 
@@ -614,6 +606,10 @@ def attn_bwd_sampled(q, k, v, kept_blocks, block: int, dout, b: int, g: int,
         Qc, dOc = _f64(q[b, pos, h]), _f64(dout[b, pos, h])
         for r0 in range(0, nk, 1024):
             r1 = min(nk, r0 + 1024)
+            # rows r0..r1-1 reach a sampled key only if it is at or before them (causal), and
+            # a sampled query only if it is one of them: otherwise they add nothing here
+            if not np.any(key_ranks < r1) and not np.any((query_ranks >= r0) & (query_ranks < r1)):
+                continue
             allowed = np.arange(r1)[None, :] <= np.arange(r0, r1)[:, None]
             O, _, P = _masked_attention(Qc[r0:r1], Kc[:r1], Vc[:r1], allowed, scale)
             Dv = (dOc[r0:r1] * O).sum(axis=1)

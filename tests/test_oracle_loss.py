@@ -66,3 +66,21 @@ def test_finite_differences_and_segment_additivity():
         assert abs(fd - dh[i, k]) < 1e-8
     parts = [oracle.lm_head_ce(h[a:a + 3], w, t[a:a + 3])[1] for a in range(0, T, 3)]
     np.testing.assert_allclose(np.concatenate(parts), rows, rtol=1e-14)
+
+
+def test_logit_gradient_against_torch_autograd():
+    # the logit gradient the oracle returns on request is the gradient of the mean loss with
+    # respect to the logits (torch autograd through cross_entropy), each row sums to zero, and
+    # dh is that gradient times w
+    rng = np.random.default_rng(5)
+    T, d, V = 6, 5, 9
+    h = rng.standard_normal((T, d))
+    w = rng.standard_normal((V, d))
+    t = rng.integers(0, V, T)
+    loss, rows, dh, g = oracle.lm_head_ce(h, w, t, with_logit_grad=True)
+    z = torch.from_numpy(h @ w.T).requires_grad_(True)
+    torch.nn.functional.cross_entropy(z, torch.from_numpy(t)).backward()
+    np.testing.assert_allclose(g, z.grad.numpy(), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(g.sum(axis=1), 0.0, atol=1e-15)
+    np.testing.assert_allclose(dh, g @ w, rtol=1e-13)
+    assert (loss, list(rows)) == (oracle.lm_head_ce(h, w, t)[0], list(oracle.lm_head_ce(h, w, t)[1]))
