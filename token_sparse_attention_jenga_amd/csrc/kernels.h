@@ -14,8 +14,10 @@ struct ScoreParams {
   float scale_log2;   // softmax scale * log2(e)
   float* lse2;        // workspace [B][Hq][S]: log2-domain row normaliser
   double* mass32;     // workspace [B][Hq][S/32]: received mass per group of keys
-  float* lpart;       // workspace, bf16 path: per (batch, head) the causal triangle of partial
-                      // log2-sums, row n (key block n) holding queries n*block .. S-1
+  float* lpart;       // workspace, bf16 path: [B][Hq][S/block][chunk] partial log2-sums of the
+                      // queries of one query chunk, row n (key block n), column i - q_begin
+  int chunk;          // bf16 path: queries per scoring chunk (a multiple of 128)
+  int q_begin, q_end; // bf16 path: the query chunk of one launch pair (set by launch_score64)
   int mass_gpb;       // mass32 groups per key block (set by launch_score)
   float* scores;      // [B][S/block]
 };
@@ -120,8 +122,9 @@ struct BwdGrid {
 // dtype: 0 = fp32 operands, 1 = bf16 operands.  Each returns hipGetLastError().
 hipError_t launch_score(const ScoreParams& p, int dtype, int D, hipStream_t st);
 hipError_t launch_select(const SelectParams& p, hipStream_t st);
-hipError_t launch_fwd(const FwdParams& p, int dtype, int D, hipStream_t st);
-hipError_t launch_bwd_segment(const BwdParams& p, int dtype, int D, hipStream_t st);
+// fp32 attention, head_dim 64 (attn_fwd.hip, attn_bwd.hip)
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t st);
+hipError_t launch_bwd_segment_f32(const BwdParams& p, hipStream_t st);
 
 // bf16 scoring with async LDS staging (score64.hip)
 hipError_t launch_score64(const ScoreParams& p, int D, hipStream_t st);

@@ -9,12 +9,18 @@
 // L_in = log2 sum_{j in n, j < i} 2^(c q_i.k_j): the exponentials that make lse2_i also make
 // every L_in, so one pass over the causal scores suffices.
 //
+// L_in can only be turned into mass once lse2_i is known, at the end of the query's pass, so
+// the queries are scored in chunks (the same idea as segment-based peak cutting): the L_in of
+// one chunk of queries are stored, turned into mass and added up before the next chunk is
+// scored.  The stored partials are chunk x S/block floats per head, linear in S.
+//
 //   k_slse64       query-major, 32 queries per wave, S^T = K Q^T per 32-key step, running max
 //                  (lazily moved): lse2_i with an fp64 running sum, and L_in per key block
 //                  (fp32 block sum, stored as a log2 when the block ends).  VALU-bound: one
 //                  exponential per score; the MFMA work is half of it or less.
-//   k_sblock_mass  per (batch, head, key block): sum_i 2^(L_in - lse2_i) over the block's row of
-//                  the triangle, fp32 groups of 4 added into fp64, fixed order.  HBM-bound.
+//   k_sblock_mass  per (batch, head, key block): sum_i 2^(L_in - lse2_i) over the chunk's queries
+//                  of the block's row, fp32 groups of 4 added into fp64, fixed order; the first
+//                  chunk stores, later chunks add in chunk order.  Memory-bound.
 #include "common.h"
 #include "kernels.h"
 #include "tiles64.h"
@@ -37,12 +43,12 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
   const int b = tl.z, h = tl.y;
   const int g = h / (p.Hq / p.Hkv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
-  const int nqt = (p.S + RG - 1) / RG;
-  const int q0 = (nqt - 1 - tl.x) * RG;                  // heaviest tiles first
+  const int nqt = (p.q_end - p.q_begin + RG - 1) / RG;
+  const int q0 = p.q_begin + (nqt - 1 - tl.x) * RG;      // heaviest tiles first
   const int qw0 = q0 + 32 * w;
-  const bool active = qw0 < p.S;                         // S is a multiple of 64
+  const bool active = qw0 < p.q_end;                     // q_end is a multiple of 64
   const int qi = qw0 + lc;
-  const int nsteps = (min(q0 + RG, p.S) - 1) / 32 + 1;
+  const int nsteps = (min(q0 + RG, p.q_end) - 1) / 32 + 1;
 
   bf16x8 qf[C::NS];
   if (active) {
@@ -67,17 +73,15 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
   float bsum = 0.f;
   const int tpb = p.block / 32;                          // key steps per block
   int in_blk = 0, blk = 0;                               // wave-uniform block position
-  // this (batch, head)'s triangle: row n at n*S - block*n(n-1)/2, queries n*block .. S-1
+  // this (batch, head)'s partials of the chunk: row n (key block n), column qi - q_begin
   const int nkb = p.S / p.block;
-  float* const lp = p.lpart + ((int64_t)b * p.Hq + h) *
-                                  ((int64_t)nkb * p.S - (int64_t)p.block * nkb * (nkb - 1) / 2);
-  int row_off = 0;                                       // row blk's offset minus blk*block
+  float* const lp = p.lpart + ((int64_t)b * p.Hq + h) * nkb * p.chunk + (qi - p.q_begin);
   // a finished block's value is stored at the start of the next step, after that step's wait
   // and before its tile loads are issued: stored right away, it would sit behind those loads
   // and the next step's wait would have to take it along
   bool pend = false;
   float pend_v = 0.f;
-  int pend_i = 0;
+  int64_t pend_i = 0;
 
   const rsrc_t rk = make_rsrc_u(kbase);
   auto issue = [&](int t, char* buf) { kplan.issue(buf, rk, (uint32_t)(32 * t * kstride)); };
@@ -127,11 +131,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
     if (++in_blk == tpb || diag) {                       // block ends here for these queries
       const float tot = half_pair_sum(bsum);             // lanes l, l^32: the two key halves
       pend_v = m_run + __builtin_amdgcn_logf(tot);       // log2; of 0, -inf: no key before i
-      pend_i = row_off + qi;
+      pend_i = (int64_t)blk * p.chunk;
       pend = true;
       bsum = 0.f;
       in_blk = 0;
-      row_off += p.S - p.block * (blk + 1);              // row blk + 1, minus (blk + 1)*block
       ++blk;
     }
   };
@@ -159,19 +162,20 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
   if (hl == 0) p.lse2[((int64_t)b * p.Hq + h) * p.S + qi] = (float)((double)m_run + log2(lsum));
 }
 
-// Received mass of key block n for one (batch, head): sum over the queries i of the block's
-// triangle row of 2^(L_in - lse2_i).  One workgroup per row; each thread adds groups of four
-// terms (fp32) into an fp64 sum, then a fixed-order reduction over the workgroup.
+// Received mass of key block n for one (batch, head) from the queries of one chunk: the sum over
+// the queries i >= n*block of the chunk of 2^(L_in - lse2_i).  One workgroup per row; each
+// thread adds groups of four terms (fp32) into an fp64 sum, then a fixed-order reduction over
+// the workgroup.  The chunk starting at query 0 stores the sum (0 for rows it does not reach),
+// later chunks add theirs, one launch after another.
 constexpr int kMassThreads = 256;
 
 __global__ __launch_bounds__(kMassThreads) void k_sblock_mass(ScoreParams p) {
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int nkb = p.S / p.block;
-  const int64_t tri = (int64_t)nkb * p.S - (int64_t)p.block * nkb * (nkb - 1) / 2;
-  const int64_t row = (int64_t)n * p.S - (int64_t)p.block * n * (n - 1) / 2;
-  const float* lrow = p.lpart + ((int64_t)b * p.Hq + h) * tri + row;
-  const float* lse = p.lse2 + ((int64_t)b * p.Hq + h) * p.S + n * p.block;
-  const int len = p.S - n * p.block;                     // a multiple of 64
+  const int start = max(p.q_begin, n * p.block);         // a multiple of 64
+  const int len = max(p.q_end - start, 0);               // a multiple of 64
+  const float* lrow = p.lpart + (((int64_t)b * p.Hq + h) * nkb + n) * p.chunk + (start - p.q_begin);
+  const float* lse = p.lse2 + ((int64_t)b * p.Hq + h) * p.S + start;
   double acc = 0.0;
   constexpr int U = 4;                                   // groups whose loads are issued together
   int i = 4 * threadIdx.x;
@@ -201,25 +205,34 @@ __global__ __launch_bounds__(kMassThreads) void k_sblock_mass(ScoreParams p) {
     double t = part[0];
 #pragma unroll
     for (int w = 1; w < kMassThreads / 64; ++w) t += part[w];
-    p.mass32[((int64_t)b * p.Hq + h) * nkb + n] = t;
+    double* m = p.mass32 + ((int64_t)b * p.Hq + h) * nkb + n;
+    if (p.q_begin == 0) *m = t;
+    else if (len > 0) *m += t;
   }
 }
 
 constexpr int SCORE_NW = 4;
 
 template <int D>
-static hipError_t launch_score64_t(const ScoreParams& p, hipStream_t st) {
+static hipError_t launch_score64_t(const ScoreParams& p0, hipStream_t st) {
   constexpr int RG = 32 * SCORE_NW;
-  hipError_t e;
-  {
-    TimedLaunch tl("k_slse64", st);
-    k_slse64<D, SCORE_NW><<<dim3((p.S + RG - 1) / RG, p.Hq, p.B), 64 * SCORE_NW, 0, st>>>(p);
+  ScoreParams p = p0;
+  for (int c0 = 0; c0 < p.S; c0 += p.chunk) {
+    p.q_begin = c0;
+    p.q_end = min(p.S, c0 + p.chunk);
+    hipError_t e;
+    {
+      TimedLaunch tl("k_slse64", st);
+      k_slse64<D, SCORE_NW><<<dim3((p.q_end - p.q_begin + RG - 1) / RG, p.Hq, p.B), 64 * SCORE_NW, 0, st>>>(p);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+    TimedLaunch tl("k_sblock_mass", st);
+    k_sblock_mass<<<dim3(p.S / p.block, p.Hq, p.B), kMassThreads, 0, st>>>(p);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  if (e != hipSuccess) return e;
-  TimedLaunch tl("k_sblock_mass", st);
-  k_sblock_mass<<<dim3(p.S / p.block, p.Hq, p.B), kMassThreads, 0, st>>>(p);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_score64(const ScoreParams& p, int D, hipStream_t st) {
