@@ -89,10 +89,14 @@ size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks
  * where P^h is the causal softmax of scale * q_i . k_j over all S tokens of head h (KV head
  * h / (Hq/Hkv)); the self term i = j is excluded as in Eq. 1.  No S x S matrix is stored.
  * bf16: one streamed pass over the causal scores yields each row's log-sum-exp and, per query
- * and key block, the log2 of the block's partial sum (S^2 / (2 block) floats per head in the
- * workspace); a second, memory-bound pass turns these into the mass per key block.  fp32: two
- * streamed passes (row log-sum-exp, then received mass per key).  The result is
- * deterministic: sums are fp64 and reduced in a fixed order.
+ * and key block, the log2 of the block's partial sum; a memory-bound pass turns these into the
+ * mass per key block.  The queries go through both passes in chunks (segment-based peak
+ * cutting, [summary] 4.4.2), so the workspace holds the partial sums of one chunk only:
+ * chunk * S/block floats per (batch, head), chunk = 128 * ceil(1024 / (B * Hq)) queries
+ * (at most S rounded up to 128) -- linear in S.  fp32: two streamed passes (row log-sum-exp,
+ * then received mass per key).  The result is deterministic: sums are fp64 and reduced in a
+ * fixed order.
+ * Returns JENGA_ERR_UNSUPPORTED when a batch row of q or k spans 4 GiB or more.
  *
  *   q            [B][S][Hq][D] (dtype, strided per q_stride)
  *   k            [B][S][Hkv][D] (dtype, strided per k_stride)

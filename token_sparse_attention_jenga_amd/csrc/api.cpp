@@ -1,6 +1,7 @@
 // C ABI of the token-sparse attention hot path: argument validation, workspace sizing,
 // launch geometry and the segment loop.  Every check happens before the first launch.
 #include <math.h>
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -13,6 +14,7 @@ namespace {
 
 constexpr int kMaxBlocks = 16384;      // selection keeps one 32-bit key per block in LDS
 constexpr size_t kAlign = 256;
+constexpr double kOffsetLimit = 4294967296.0;   // 32-bit buffer-resource offsets
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -35,7 +37,19 @@ int check_problem(const jenga_problem* p, bool need_qkv_strides) {
     for (int t = 0; t < 3; ++t)
       for (int i = 0; i < 3; ++i)
         if (st[t][i] < 0 || (st[t][i] * es) % 16 != 0) return JENGA_ERR_INVALID_ARG;
+    // The kernels address Q, K and V through buffer resources whose base is a batch row and
+    // whose per-lane offsets are 32-bit: every byte of a batch row they can touch (any token,
+    // any head) must lie below 4 GiB from that row's start.
+    for (int t = 0; t < 3; ++t) {
+      const double heads = t == 0 ? p->n_heads_q : p->n_heads_kv;
+      const double extent = ((double)(p->seq_len - 1) * (double)st[t][1] +
+                             (heads - 1.0) * (double)st[t][2] + (double)p->head_dim) * es;
+      if (extent >= kOffsetLimit) return JENGA_ERR_UNSUPPORTED;
+    }
   }
+  // fp32 residual and gradient rows of one batch row, and the per-head score workspace, are
+  // indexed with the same 32-bit offsets
+  if ((double)p->seq_len * p->n_heads_q * p->head_dim * 4.0 >= kOffsetLimit) return JENGA_ERR_UNSUPPORTED;
   return JENGA_OK;
 }
 
@@ -93,19 +107,31 @@ size_t score_eq2_ws_bytes(const jenga_problem* p) {
   return align_up((size_t)p->batch * nkb * nkb * sizeof(float));
 }
 
-// per (batch, head): the causal triangle of key-block partial log2-sums (bf16 path)
-size_t score_tri_elems(const jenga_problem* p) {
-  const size_t nkb = p->seq_len / p->block;
-  return nkb * p->seq_len - (size_t)p->block * nkb * (nkb - 1) / 2;
+// bf16 scoring runs in chunks of queries; each chunk's partial log2-sums (one per query and key
+// block) are turned into mass before the next chunk.  A chunk holds enough 128-query tiles for
+// at least 1024 workgroups (four per compute unit), or S rounded up to the tile if that is
+// less, so the stored partials are chunk x S/block floats per (batch, head): linear in S.
+constexpr int kScoreTile = 128;
+constexpr int kScoreMinWorkgroups = 1024;
+
+int score_chunk(const jenga_problem* p) {
+  const int64_t heads = (int64_t)p->batch * p->n_heads_q;
+  const int64_t tiles = (kScoreMinWorkgroups + heads - 1) / heads;
+  const int64_t s_up = ((int64_t)p->seq_len + kScoreTile - 1) / kScoreTile * kScoreTile;
+  return (int)std::min<int64_t>(tiles * kScoreTile, s_up);
+}
+
+size_t score_part_elems(const jenga_problem* p) {        // per (batch, head)
+  return (size_t)(p->seq_len / p->block) * score_chunk(p);
 }
 
 size_t score_ws_bytes(const jenga_problem* p) {
   const size_t lse = (size_t)p->batch * p->n_heads_q * p->seq_len * sizeof(float);
   const size_t mass = (size_t)p->batch * p->n_heads_q * (p->seq_len / 32) * sizeof(double);
-  const size_t tri = p->dtype == JENGA_DTYPE_BF16
-                         ? (size_t)p->batch * p->n_heads_q * score_tri_elems(p) * sizeof(float)
-                         : 0;
-  return align_up(lse) + align_up(mass) + align_up(tri);
+  const size_t part = p->dtype == JENGA_DTYPE_BF16
+                          ? (size_t)p->batch * p->n_heads_q * score_part_elems(p) * sizeof(float)
+                          : 0;
+  return align_up(lse) + align_up(mass) + align_up(part);
 }
 
 int check_proj(const jenga_proj_problem* p, const void* in, const void* w, const int32_t* kept,
@@ -272,6 +298,9 @@ int jenga_score_blocks(const jenga_problem* p, const void* q, const void* k, flo
                         align_up((size_t)p->batch * p->n_heads_q * p->seq_len * sizeof(float)));
   sp.lpart = (float*)((char*)sp.mass32 +
                       align_up((size_t)p->batch * p->n_heads_q * (p->seq_len / 32) * sizeof(double)));
+  sp.chunk = score_chunk(p);
+  sp.q_begin = 0;
+  sp.q_end = p->seq_len;
   sp.mass_gpb = 0;
   sp.scores = block_scores;
   if (jenga::launch_score(sp, p->dtype, p->head_dim, (hipStream_t)stream) != hipSuccess)
@@ -375,7 +404,7 @@ int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, 
   fp.vtp = workspace;
   const hipError_t e = p->dtype == JENGA_DTYPE_BF16
                            ? jenga::launch_fwd64(fp, p->head_dim, (hipStream_t)stream)
-                           : jenga::launch_fwd(fp, p->dtype, p->head_dim, (hipStream_t)stream);
+                           : jenga::launch_fwd_f32(fp, (hipStream_t)stream);
   if (e != hipSuccess) return JENGA_ERR_LAUNCH;
   return JENGA_OK;
 }
@@ -437,7 +466,7 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
     if ((int64_t)s * L >= ncap) break;
     bp.seg = s;
     const hipError_t e = fast ? jenga::launch_bwd64_segment(bp, p->head_dim, (hipStream_t)stream)
-                              : jenga::launch_bwd_segment(bp, p->dtype, p->head_dim, (hipStream_t)stream);
+                              : jenga::launch_bwd_segment_f32(bp, (hipStream_t)stream);
     if (e != hipSuccess) return JENGA_ERR_LAUNCH;
   }
   return JENGA_OK;
