@@ -1,4 +1,5 @@
-// Segmented backward of the token-sparse attention for gfx950.
+// Segmented backward of the token-sparse attention for gfx950, fp32 operands (head_dim 64,
+// fp32 MFMA); the bf16 backward is attn64.hip.
 //
 // Jenga (papercache notes, §4.4, segment-based peak cutting: the sequence is processed as N
 // segments one after the other, each segment's transient activations are discarded once its
@@ -23,11 +24,7 @@ namespace jenga {
 
 template <typename T>
 __device__ inline typename Mfma<T>::frag ld_frag_b(const char* p) {
-  if constexpr (sizeof(T) == 2) {
-    return *(const bf16x8*)p;
-  } else {
-    return *(const float*)p;
-  }
+  return *(const float*)p;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -52,19 +49,9 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdParams p) {
     const f32x4 dov = *(const f32x4*)(p.dout + (((int64_t)b * p.S + pos) * p.Hq + h) * D + d0);
     const int64_t oidx = (((int64_t)b * p.ncap + r) * p.Hq + h) * D + d0;
     const int64_t widx = (((int64_t)b * p.seg_len + rl) * p.Hq + h) * D + d0;
-    if constexpr (sizeof(T) == 2) {
-      const u32x2 ow = *(const u32x2*)((const char*)p.o_saved + oidx * 2);
-      dot = dov[0] * bf16_lo(ow[0]) + dov[1] * bf16_hi(ow[0]) + dov[2] * bf16_lo(ow[1]) +
-            dov[3] * bf16_hi(ow[1]);
-      u32x2 dw;
-      dw[0] = pack_bf16x2(dov[0], dov[1]);
-      dw[1] = pack_bf16x2(dov[2], dov[3]);
-      *(u32x2*)((char*)p.wsdO + widx * 2) = dw;
-    } else {
-      const f32x4 ov = *(const f32x4*)((const char*)p.o_saved + oidx * 4);
-      dot = dov[0] * ov[0] + dov[1] * ov[1] + dov[2] * ov[2] + dov[3] * ov[3];
-      *(f32x4*)((char*)p.wsdO + widx * 4) = dov;
-    }
+    const f32x4 ov = *(const f32x4*)((const char*)p.o_saved + oidx * 4);
+    dot = dov[0] * ov[0] + dov[1] * ov[1] + dov[2] * ov[2] + dov[3] * ov[3];
+    *(f32x4*)((char*)p.wsdO + widx * 4) = dov;
   }
 #pragma unroll
   for (int off = TPR / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
@@ -209,35 +196,16 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(BwdParams p) {
           }
         }
         // dV += P^T dO, dK += dS^T Q  (M = keys, N = head_dim, reduction over queries)
-        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int qb = j >> 1, jj = j & 1;
-            const bf16x8 pf = to_frag8(sacc[qb][8 * jj + 0], sacc[qb][8 * jj + 1], sacc[qb][8 * jj + 2],
-                                       sacc[qb][8 * jj + 3], sacc[qb][8 * jj + 4], sacc[qb][8 * jj + 5],
-                                       sacc[qb][8 * jj + 6], sacc[qb][8 * jj + 7]);
-            const bf16x8 sf = to_frag8(pacc[qb][8 * jj + 0], pacc[qb][8 * jj + 1], pacc[qb][8 * jj + 2],
-                                       pacc[qb][8 * jj + 3], pacc[qb][8 * jj + 4], pacc[qb][8 * jj + 5],
-                                       pacc[qb][8 * jj + 6], pacc[qb][8 * jj + 7]);
-            const int r0 = qb * 32 + 16 * jj + 4 * hl;
+        for (int t = 0; t < 32; ++t) {
+          const int qb = t >> 4, r = t & 15;
+          const int ql = qb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
 #pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-              dva[db] = M::mma(pf, lds_frag_tr(dOls, C::LDQ, r0, r0 + 8, db * 32), dva[db]);
-              dka[db] = M::mma(sf, lds_frag_tr(Qls, C::LDQ, r0, r0 + 8, db * 32), dka[db]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < 32; ++t) {
-            const int qb = t >> 4, r = t & 15;
-            const int ql = qb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-              const float bdo = *(const float*)(dOl + ql * C::LDQ + (db * 32 + lc) * 4);
-              const float bq = *(const float*)(Ql + ql * C::LDQ + (db * 32 + lc) * 4);
-              dva[db] = M::mma(sacc[qb][r], bdo, dva[db]);
-              dka[db] = M::mma(pacc[qb][r], bq, dka[db]);
-            }
+          for (int db = 0; db < C::NDB; ++db) {
+            const float bdo = *(const float*)(dOl + ql * C::LDQ + (db * 32 + lc) * 4);
+            const float bq = *(const float*)(Ql + ql * C::LDQ + (db * 32 + lc) * 4);
+            dva[db] = M::mma(sacc[qb][r], bdo, dva[db]);
+            dka[db] = M::mma(pacc[qb][r], bq, dka[db]);
           }
         }
         // dS^T -> LDS: row = key (32w + lc), 4 consecutive queries per store
@@ -247,19 +215,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(BwdParams p) {
           for (int rg = 0; rg < 4; ++rg) {
             const int qcol = qb * 32 + 8 * rg + 4 * hl;
             char* dst = dSl + (32 * w + lc) * C::LDS_ + qcol * C::ES;
-            if constexpr (sizeof(T) == 2) {
-              u32x2 pw;
-              pw[0] = pack_bf16x2(pacc[qb][4 * rg + 0], pacc[qb][4 * rg + 1]);
-              pw[1] = pack_bf16x2(pacc[qb][4 * rg + 2], pacc[qb][4 * rg + 3]);
-              *(u32x2*)dst = pw;
-            } else {
-              f32x4 y;
-              y[0] = pacc[qb][4 * rg + 0];
-              y[1] = pacc[qb][4 * rg + 1];
-              y[2] = pacc[qb][4 * rg + 2];
-              y[3] = pacc[qb][4 * rg + 3];
-              *(f32x4*)dst = y;
-            }
+            f32x4 y;
+            y[0] = pacc[qb][4 * rg + 0];
+            y[1] = pacc[qb][4 * rg + 1];
+            y[2] = pacc[qb][4 * rg + 2];
+            y[3] = pacc[qb][4 * rg + 3];
+            *(f32x4*)dst = y;
           }
         }
       } else {
@@ -275,23 +236,14 @@ __global__ __launch_bounds__(256, 1) void k_bwd_main(BwdParams p) {
       for (int item = w; item < 2 * C::NDB; item += 4) {
         const int qb = item / C::NDB, db = item % C::NDB;
         f32x16 acc = zero16();
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-          for (int ks = 0; ks < C::BKC / 16; ++ks) {
-            const int r0 = ks * 16 + 8 * hl;
-            const bf16x8 a = lds_frag_tr(dSls, C::LDS_, r0, r0 + 4, qb * 32);
-            const bf16x8 bk = lds_frag_tr(Kls, C::LDK, r0, r0 + 4, db * 32);
-            acc = M::mma(a, bk, acc);
-          }
-        } else {
 #pragma unroll 8
-          for (int ks = 0; ks < C::BKC / 2; ++ks) {
-            const int key = 2 * ks + hl;
-            const float a = *(const float*)(dSl + key * C::LDS_ + (qb * 32 + lc) * 4);
-            const float bk = *(const float*)(smem + C::K_OFF + key * C::LDK + (db * 32 + lc) * 4);
-            acc = M::mma(a, bk, acc);
-          }
+        for (int ks = 0; ks < C::BKC / 2; ++ks) {
+          const int key = 2 * ks + hl;
+          const float a = *(const float*)(dSl + key * C::LDS_ + (qb * 32 + lc) * 4);
+          const float bk = *(const float*)(smem + C::K_OFF + key * C::LDK + (db * 32 + lc) * 4);
+          acc = M::mma(a, bk, acc);
         }
+
         float* dqb = p.dq + (((int64_t)b * p.S + qpos0) * p.Hq + h) * D + db * 32 + lc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -331,9 +283,6 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_segment(const BwdParams& p, int dtype, int D, hipStream_t st) {
-  if (dtype == 1) return D == 64 ? launch_bwd_t<bf16, 64>(p, st) : launch_bwd_t<bf16, 128>(p, st);
-  return launch_bwd_t<float, 64>(p, st);     // fp32 operands: head_dim 64 only
-}
-
+// fp32 operands, head_dim 64 (the bf16 backward is attn64.hip)
+hipError_t launch_bwd_segment_f32(const BwdParams& p, hipStream_t st) { return launch_bwd_t<float, 64>(p, st); }
 }  // namespace jenga

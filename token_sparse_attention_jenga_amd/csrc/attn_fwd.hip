@@ -1,4 +1,5 @@
-// Permutation-free token-sparse causal attention forward for gfx950.
+// Permutation-free token-sparse causal attention forward for gfx950, fp32 operands
+// (head_dim 64, fp32 MFMA); the bf16 forward is attn64.hip.
 //
 // Jenga (papercache notes, §4.4, permutation-free token movement; Fig. 9): kept tokens are
 // read straight from the full-length Q/K/V through the kept-block index list (no gathered
@@ -8,9 +9,8 @@
 // One workgroup = 4 waves = 128 kept query ranks of one query head.  Each wave owns 32
 // queries and computes S^T = K Q^T (keys x queries) so that every lane holds one query's
 // column: the online-softmax row statistics are lane-local plus one exchange with lane
-// l^32.  O^T = V^T P^T accumulates in registers; P^T leaves the S^T accumulator directly
-// as the MFMA B operand, and V^T is read from a row-major LDS tile with the gfx950
-// transpose read, with the key order permuted to match the accumulator layout.
+// l^32.  O^T = V^T P^T accumulates in registers: each fp32 MFMA takes one key's P^T value
+// straight from the S^T accumulator and that key's V values from the row-major LDS tile.
 // K/V tiles of 64 kept keys are double-buffered in LDS; a tile is one contiguous run of
 // token positions because blocks are multiples of 64 tokens.
 #include "common.h"
@@ -20,11 +20,7 @@ namespace jenga {
 
 template <typename T>
 __device__ inline typename Mfma<T>::frag ld_frag(const char* p) {
-  if constexpr (sizeof(T) == 2) {
-    return *(const bf16x8*)p;
-  } else {
-    return *(const float*)p;
-  }
+  return *(const float*)p;
 }
 
 template <typename T, int D>
@@ -165,28 +161,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
       const LDS_AS char* vls = (const LDS_AS char*)vl;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const bf16x8 pf = to_frag8(st[kb][8 * j + 0], st[kb][8 * j + 1], st[kb][8 * j + 2],
-                                       st[kb][8 * j + 3], st[kb][8 * j + 4], st[kb][8 * j + 5],
-                                       st[kb][8 * j + 6], st[kb][8 * j + 7]);
-            const int r0 = kb * 32 + 16 * j + 4 * hl;
+        for (int t = 0; t < 16; ++t) {
+          const int key = kb * 32 + 8 * (t >> 2) + 4 * hl + (t & 3);
 #pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-              const bf16x8 va = lds_frag_tr(vls, C::LDV, r0, r0 + 8, db * 32);
-              o[db] = M::mma(va, pf, o[db]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int key = kb * 32 + 8 * (t >> 2) + 4 * hl + (t & 3);
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-              const float va = *(const float*)(vl + key * C::LDV + (db * 32 + lc) * 4);
-              o[db] = M::mma(va, st[kb][t], o[db]);
-            }
+          for (int db = 0; db < C::NDB; ++db) {
+            const float va = *(const float*)(vl + key * C::LDV + (db * 32 + lc) * 4);
+            o[db] = M::mma(va, st[kb][t], o[db]);
           }
         }
       }
@@ -214,19 +195,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
       x[2] += v2;
       x[3] += v3;
       *(f32x4*)(rrow + d0) = x;
-      if constexpr (sizeof(T) == 2) {
-        u32x2 pw;
-        pw[0] = pack_bf16x2(v0, v1);
-        pw[1] = pack_bf16x2(v2, v3);
-        *(u32x2*)(orow + d0 * 2) = pw;
-      } else {
-        f32x4 y;
-        y[0] = v0;
-        y[1] = v1;
-        y[2] = v2;
-        y[3] = v3;
-        *(f32x4*)(orow + d0 * 4) = y;
-      }
+      f32x4 y;
+      y[0] = v0;
+      y[1] = v1;
+      y[2] = v2;
+      y[3] = v3;
+      *(f32x4*)(orow + d0 * 4) = y;
     }
   }
   if (hl == 0) p.lse[((int64_t)b * p.Hq + h) * p.ncap + qr] = (m_run + log2f(l_run)) * kLn2;
@@ -240,9 +214,6 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdParams& p, int dtype, int D, hipStream_t st) {
-  if (dtype == 1) return D == 64 ? launch_fwd_t<bf16, 64>(p, st) : launch_fwd_t<bf16, 128>(p, st);
-  return launch_fwd_t<float, 64>(p, st);      // fp32 operands: head_dim 64 only
-}
-
+// fp32 operands, head_dim 64 (the bf16 forward is attn64.hip)
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t st) { return launch_fwd_t<float, 64>(p, st); }
 }  // namespace jenga

@@ -21,11 +21,7 @@ namespace jenga {
 
 template <typename T>
 __device__ inline typename Mfma<T>::frag ld_frag_s(const char* p) {
-  if constexpr (sizeof(T) == 2) {
-    return *(const bf16x8*)p;
-  } else {
-    return *(const float*)p;
-  }
+  return *(const float*)p;
 }
 
 template <typename T, int D>
@@ -276,5 +272,4 @@ hipError_t launch_score(const ScoreParams& p0, int dtype, int D, hipStream_t st)
   p.mass_gpb = p.block / 32;             // fp32: mass per 32-key group
   return launch_score_t<float, 64>(p, st);    // fp32 operands: head_dim 64 only
 }
-
 }  // namespace jenga
