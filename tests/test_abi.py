@@ -83,6 +83,37 @@ def test_score_validation(J):
     assert _score(J, bad) == J.JENGA_ERR_INVALID_ARG
 
 
+def test_offsets_past_4gib_rejected(J):
+    # the kernels address each batch row of q / k / v through 32-bit buffer offsets, and the
+    # fp32 residual and gradient rows of a batch row with 32-bit offsets too: a problem whose
+    # rows span 4 GiB or more is refused before any launch, in every entry point
+    def calls(pp):
+        # (a zero-byte workspace: a problem that passes the shape checks stops at the workspace
+        # check, so nothing is ever launched on these fake pointers)
+        return (J.lib.jenga_score_blocks(ctypes.byref(pp), FAKE, FAKE, FAKE, FAKE, 0, None),
+                J.lib.jenga_sparse_attn_fwd(ctypes.byref(pp), FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE,
+                                            FAKE, FAKE, FAKE, 0, None),
+                J.lib.jenga_sparse_attn_bwd_segmented(ctypes.byref(pp), FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                                                      FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE,
+                                                      0, None))
+    U = J.JENGA_ERR_UNSUPPORTED
+    # 512K tokens of 32 x 128 bf16 heads: 4 GiB per batch row of q
+    assert calls(_problem(J, S=1 << 19, Hq=32, Hkv=32, D=128, block=128, dtype=1)) == (U, U, U)
+    # K as a view into a packed QKV tensor (3 * 32 * 128 bf16 per token, 24 KiB): 171K tokens
+    # already span 4 GiB, though K alone would not
+    packed = _problem(J, S=176128, Hq=32, Hkv=32, D=128, block=128, dtype=1)
+    for name in ("q_stride", "k_stride", "v_stride"):
+        getattr(packed, name)[1] = 3 * 32 * 128
+    assert calls(packed) == (U, U, U)
+    # the fp32 residual rows alone: 256K tokens of 32 x 128 heads is 4 GiB of fp32 per batch row,
+    # even though the bf16 q / k / v rows are half that
+    assert calls(_problem(J, S=1 << 18, Hq=32, Hkv=8, D=128, block=128, dtype=1)) == (U, U, U)
+    # just below every limit the shape checks pass and the workspace check decides
+    ok = _problem(J, S=(1 << 18) - 128, Hq=32, Hkv=8, D=128, block=128, dtype=1)
+    W = J.JENGA_ERR_WORKSPACE
+    assert calls(ok) == (W, W, W)
+
+
 def test_select_validation(J):
     p = _problem(J)
     f = lambda mode=0, param=0.5, flags=0, s=FAKE: J.lib.jenga_select_blocks(
@@ -138,20 +169,27 @@ def test_workspace_scales_with_segments_and_kept_blocks(J):
 
 def test_score_workspace(J):
     # lse2 rows (fp32) and mass slots (fp64, one per 32 keys), each rounded to 256 bytes; the
-    # bf16 path adds, per (batch, head), the causal triangle of key-block partial log2-sums:
-    # row n holds the queries n*block .. S-1, S*nKB - block*nKB*(nKB-1)/2 floats in all
+    # bf16 path adds the partial log2-sums of one query chunk: chunk * nKB floats per (batch,
+    # head), chunk = 128 * ceil(1024 / (B * Hq)) queries, at most S rounded up to 128
     up = lambda x: (x + 255) // 256 * 256
-    for B, S, Hq, block in ((1, 32768, 32, 128), (2, 4096, 8, 64), (1, 576, 2, 192)):
+    for B, S, Hq, block in ((1, 32768, 32, 128), (2, 4096, 8, 64), (1, 576, 2, 192),
+                            (1, 131072, 32, 128), (1, 16384, 32, 64)):
         nkb = S // block
-        tri = S * nkb - block * nkb * (nkb - 1) // 2
+        chunk = min(128 * -(-1024 // (B * Hq)), -(-S // 128) * 128)
         base = up(B * Hq * S * 4) + up(B * Hq * (S // 32) * 8)
         p16 = _problem(J, B=B, S=S, Hq=Hq, Hkv=Hq, D=128, block=block, dtype=1)
-        assert J.workspace_bytes(p16, J.JENGA_OP_SCORE) == base + up(B * Hq * tri * 4)
+        assert J.workspace_bytes(p16, J.JENGA_OP_SCORE) == base + up(B * Hq * nkb * chunk * 4)
         p32 = _problem(J, B=B, S=S, Hq=Hq, Hkv=Hq, D=64, block=block, dtype=0)
         assert J.workspace_bytes(p32, J.JENGA_OP_SCORE) == base
-    # 32K tokens, 32 heads, block 128: 514 MiB of partial sums beside 4.25 MiB of rows and slots
+    # 32K tokens, 32 heads, block 128: chunks of 4096 queries, 128 MiB of partial sums beside
+    # 4.25 MiB of rows and slots (the whole causal triangle would be 514 MiB)
     c5 = _problem(J, S=32768, Hq=32, Hkv=32, D=128, block=128, dtype=1)
-    assert J.workspace_bytes(c5, J.JENGA_OP_SCORE) == 4 * 2**20 + 2**18 + 32 * 4210688 * 4
+    assert J.workspace_bytes(c5, J.JENGA_OP_SCORE) == 4 * 2**20 + 2**18 + 128 * 2**20
+    # linear in S: at four times the tokens the partial sums take four times the bytes
+    c5x4 = _problem(J, S=131072, Hq=32, Hkv=32, D=128, block=128, dtype=1)
+    rows = lambda S: S * 32 * 4 + S // 32 * 32 * 8
+    assert (J.workspace_bytes(c5x4, J.JENGA_OP_SCORE) - rows(131072)
+            == 4 * (J.workspace_bytes(c5, J.JENGA_OP_SCORE) - rows(32768)))
 
 
 def test_timing_calls_without_gpu_work(J):
@@ -248,3 +286,52 @@ def test_loss_validation_and_workspace(J):
     assert f(wsb=w8 - 1) == J.JENGA_ERR_WORKSPACE
     assert f(pp=J.loss_problem(64, 4096, 32000, 3)) == J.JENGA_ERR_INVALID_ARG   # > T/32 segments
     assert f(pp=J.loss_problem(64, 4000, 32000, 1)) == J.JENGA_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_views_dtypes_and_shapes(J):
+    # the binding checks every dense argument before a pointer reaches the library: a view, a
+    # wrong dtype or a wrong shape raises ValueError (CPU tensors: these checks come first)
+    import torch
+    B, S, Hq, Hkv, D, block, maxk = 1, 256, 4, 2, 64, 64, 2
+    q = torch.zeros((B, S, Hq, D), dtype=torch.bfloat16)
+    k = torch.zeros((B, S, Hkv, D), dtype=torch.bfloat16)
+    p = J.make_problem(q, k, k, block)
+    kept = torch.zeros((B, S // block), dtype=torch.int32)
+    nk = torch.zeros((B,), dtype=torch.int32)
+    resid = torch.zeros((B, S, Hq, D), dtype=torch.float32)
+    o = torch.zeros((B, maxk * block, Hq, D), dtype=torch.bfloat16)
+    lse = torch.zeros((B, Hq, maxk * block), dtype=torch.float32)
+    fwd = lambda **kw: J.jenga_sparse_attn_fwd(p, q, k, k, kw.get("kept", kept), kw.get("nk", nk), maxk,
+                                               kw.get("resid", resid), kw.get("o", o), kw.get("lse", lse))
+    with pytest.raises(ValueError, match="resid: dtype"):
+        fwd(resid=resid.to(torch.bfloat16))
+    with pytest.raises(ValueError, match="resid: must be contiguous"):
+        fwd(resid=torch.zeros((B, Hq, S, D)).transpose(1, 2))
+    with pytest.raises(ValueError, match="o_saved: shape"):
+        fwd(o=o[:, :block])
+    with pytest.raises(ValueError, match="lse: shape"):
+        fwd(lse=lse.transpose(1, 2))
+    with pytest.raises(ValueError, match="kept_idx: dtype"):
+        fwd(kept=kept.long())
+    with pytest.raises(ValueError, match="n_kept: shape"):
+        fwd(nk=torch.zeros((2,), dtype=torch.int32))
+    g = torch.zeros((B, S, Hq, D), dtype=torch.float32)
+    gk = torch.zeros((B, S, Hkv, D), dtype=torch.float32)
+    bwd = lambda **kw: J.jenga_sparse_attn_bwd_segmented(
+        p, q, k, k, kept, nk, maxk, o, lse, kw.get("dout", g), kw.get("dq", g), kw.get("dk", gk),
+        kw.get("dv", gk), 1, torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="dk: shape"):
+        bwd(dk=g)
+    with pytest.raises(ValueError, match="dout: dtype"):
+        bwd(dout=g.double())
+    with pytest.raises(ValueError, match="dq: must be contiguous"):
+        bwd(dq=torch.zeros((B, S, D, Hq)).transpose(2, 3))
+    with pytest.raises(ValueError, match="block_scores: shape"):
+        J.jenga_score_blocks(p, q, k, torch.zeros((B, 3)), torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="share one dtype"):
+        J.make_problem(q, k.float(), k, block)
+    with pytest.raises(ValueError, match="do not match"):
+        J.make_problem(q, k[:, :128], k, block)
+    with pytest.raises(ValueError, match="targets: dtype"):
+        J.lm_head_ce(torch.zeros((64, 128), dtype=torch.bfloat16), torch.zeros((256, 128), dtype=torch.bfloat16),
+                     torch.zeros((128, 256), dtype=torch.bfloat16), torch.zeros(64, dtype=torch.int64))

@@ -153,10 +153,52 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _dense(name: str, t, shape, dtype=None) -> None:
+    """The library indexes this argument as a dense tensor of exactly this shape: refuse views,
+    other dtypes and other shapes here, before a pointer reaches a kernel."""
+    if t is None:
+        raise ValueError(f"{name}: missing")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _on_device(**ts) -> None:
+    """Every tensor argument lives in device memory (checked after shapes and dtypes)."""
+    for name, t in ts.items():
+        if t is not None and t.numel() and t.device.type != "cuda":
+            raise ValueError(f"{name}: must be a device tensor")
+
+
+def _f32():
+    import torch
+    return torch.float32
+
+
+def _i32():
+    import torch
+    return torch.int32
+
+
+def _ws_check(workspace) -> None:
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace: must be contiguous")
+
+
 def make_problem(q, k, v=None, block: int = 64, scale: float = 0.0) -> JengaProblem:
     """Problem descriptor from BSHD tensors (views allowed: strides are passed through)."""
+    if q.dim() != 4 or k.dim() != 4 or (v is not None and v.dim() != 4):
+        raise ValueError("q, k, v: expected [batch, tokens, heads, head_dim] tensors")
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
+    if tuple(k.shape) != (B, S, Hkv, D) or (v is not None and tuple(v.shape) != (B, S, Hkv, D)):
+        raise ValueError(f"k, v: shapes {tuple(k.shape)}, {None if v is None else tuple(v.shape)} "
+                         f"do not match q {tuple(q.shape)}")
+    if k.dtype != q.dtype or (v is not None and v.dtype != q.dtype):
+        raise ValueError("q, k, v: must share one dtype")
     p = JengaProblem()
     p.batch, p.seq_len, p.n_heads_q, p.n_heads_kv, p.head_dim, p.block = B, S, Hq, Hkv, D, block
     p.dtype = _dtype_code(q)
@@ -193,7 +235,14 @@ def alloc_workspace(nbytes: int, device):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+def _nkb(p: JengaProblem) -> int:
+    return p.seq_len // p.block if p.block > 0 else 0
+
+
 def jenga_score_blocks(p: JengaProblem, q, k, block_scores, workspace, stream=None) -> None:
+    _dense("block_scores", block_scores, (p.batch, _nkb(p)), _f32())
+    _ws_check(workspace)
+    _on_device(q=q, k=k, block_scores=block_scores, workspace=workspace)
     st = lib.jenga_score_blocks(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(block_scores),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream))
@@ -201,6 +250,9 @@ def jenga_score_blocks(p: JengaProblem, q, k, block_scores, workspace, stream=No
 
 
 def jenga_score_blocks_eq2(p: JengaProblem, q, k, block_scores, workspace, stream=None) -> None:
+    _dense("block_scores", block_scores, (p.batch, _nkb(p)), _f32())
+    _ws_check(workspace)
+    _on_device(q=q, k=k, block_scores=block_scores, workspace=workspace)
     st = lib.jenga_score_blocks_eq2(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(block_scores),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream))
@@ -209,6 +261,10 @@ def jenga_score_blocks_eq2(p: JengaProblem, q, k, block_scores, workspace, strea
 
 def jenga_select_blocks(p: JengaProblem, block_scores, mode: int, param: float, flags: int,
                         kept_idx, n_kept, stream=None) -> None:
+    _dense("block_scores", block_scores, (p.batch, _nkb(p)), _f32())
+    _dense("kept_idx", kept_idx, (p.batch, _nkb(p)), _i32())
+    _dense("n_kept", n_kept, (p.batch,), _i32())
+    _on_device(block_scores=block_scores, kept_idx=kept_idx, n_kept=n_kept)
     st = lib.jenga_select_blocks(ctypes.byref(p), _ptr(block_scores), int(mode),
                                  ctypes.c_float(param), int(flags), _ptr(kept_idx), _ptr(n_kept),
                                  _stream(stream))
@@ -217,6 +273,16 @@ def jenga_select_blocks(p: JengaProblem, block_scores, mode: int, param: float, 
 
 def jenga_sparse_attn_fwd(p: JengaProblem, q, k, v, kept_idx, n_kept, max_kept_blocks: int,
                           resid, o_saved, lse, workspace=None, stream=None) -> None:
+    B, S, Hq, D, Hkv = p.batch, p.seq_len, p.n_heads_q, p.head_dim, p.n_heads_kv
+    ncap = int(max_kept_blocks) * p.block
+    _dense("kept_idx", kept_idx, (B, _nkb(p)), _i32())
+    _dense("n_kept", n_kept, (B,), _i32())
+    _dense("resid", resid, (B, S, Hq, D), _f32())
+    _dense("o_saved", o_saved, (B, ncap, Hq, D), q.dtype)
+    _dense("lse", lse, (B, Hq, ncap), _f32())
+    _ws_check(workspace)
+    _on_device(q=q, k=k, v=v, kept_idx=kept_idx, n_kept=n_kept, resid=resid, o_saved=o_saved,
+               lse=lse, workspace=workspace)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.jenga_sparse_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_idx),
                                    _ptr(n_kept), int(max_kept_blocks), _ptr(resid), _ptr(o_saved),
@@ -227,6 +293,19 @@ def jenga_sparse_attn_fwd(p: JengaProblem, q, k, v, kept_idx, n_kept, max_kept_b
 def jenga_sparse_attn_bwd_segmented(p: JengaProblem, q, k, v, kept_idx, n_kept,
                                     max_kept_blocks: int, o_saved, lse, dout, dq, dk, dv,
                                     n_segments: int, workspace, stream=None) -> None:
+    B, S, Hq, D, Hkv = p.batch, p.seq_len, p.n_heads_q, p.head_dim, p.n_heads_kv
+    ncap = int(max_kept_blocks) * p.block
+    _dense("kept_idx", kept_idx, (B, _nkb(p)), _i32())
+    _dense("n_kept", n_kept, (B,), _i32())
+    _dense("o_saved", o_saved, (B, ncap, Hq, D), q.dtype)
+    _dense("lse", lse, (B, Hq, ncap), _f32())
+    _dense("dout", dout, (B, S, Hq, D), _f32())
+    _dense("dq", dq, (B, S, Hq, D), _f32())
+    _dense("dk", dk, (B, S, Hkv, D), _f32())
+    _dense("dv", dv, (B, S, Hkv, D), _f32())
+    _ws_check(workspace)
+    _on_device(q=q, k=k, v=v, kept_idx=kept_idx, n_kept=n_kept, o_saved=o_saved, lse=lse,
+               dout=dout, dq=dq, dk=dk, dv=dv, workspace=workspace)
     st = lib.jenga_sparse_attn_bwd_segmented(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_idx), _ptr(n_kept),
         int(max_kept_blocks), _ptr(o_saved), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -309,6 +388,17 @@ def sparse_attn_bwd(q, k, v, kept_idx, n_kept, max_kept_blocks: int, block: int,
 def make_proj_problem(inp, w, out, block: int, seq_len: int) -> JengaProjProblem:
     """inp: [B, rows, K] bf16 (rows = S for the gathered input, Ncap for compact rows);
     w: [N, K] bf16; out: [B, rows_out, N] (bf16 compact or fp32 residual)."""
+    import torch
+    if inp.dim() != 3 or out.dim() != 3 or w.dim() != 2:
+        raise ValueError("projection: inp [B, rows, K], w [N, K] and out [B, rows, N] expected")
+    if inp.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("projection: inp and w must be bf16")
+    _dense("w", w, (w.shape[0], inp.shape[2]), torch.bfloat16)
+    if out.shape[0] != inp.shape[0] or out.shape[2] != w.shape[0]:
+        raise ValueError(f"projection: out {tuple(out.shape)} does not match inp {tuple(inp.shape)} "
+                         f"and w {tuple(w.shape)}")
+    if inp.stride(2) != 1 or out.stride(2) != 1:
+        raise ValueError("projection: the feature dimension of inp and out must be contiguous")
     p = JengaProjProblem()
     p.batch, p.seq_len, p.block = inp.shape[0], int(seq_len), int(block)
     p.in_features, p.out_features = inp.shape[2], w.shape[0]
@@ -323,16 +413,28 @@ def proj_gather(x, w, kept_idx, n_kept, max_kept_blocks: int, block: int, stream
     B, S, _ = x.shape
     y = torch.empty((B, max_kept_blocks * block, w.shape[0]), dtype=torch.bfloat16, device=x.device)
     p = make_proj_problem(x, w, y, block, S)
+    _kept_check(kept_idx, n_kept, B, S // block)
     st = lib.jenga_proj_gather(ctypes.byref(p), _ptr(x), _ptr(w), _ptr(kept_idx), _ptr(n_kept),
                                int(max_kept_blocks), _ptr(y), _stream(stream))
     _check("jenga_proj_gather", st)
     return y
 
 
+def _kept_check(kept_idx, n_kept, B: int, nkb: int) -> None:
+    _dense("kept_idx", kept_idx, (B, nkb), _i32())
+    _dense("n_kept", n_kept, (B,), _i32())
+    _on_device(kept_idx=kept_idx, n_kept=n_kept)
+
+
 def proj_scatter_add(y, w, kept_idx, n_kept, max_kept_blocks: int, block: int, resid,
                      stream=None) -> None:
     """resid[b, pos(r)] += y[b, r] @ w^T at the kept rows (resid fp32 [B, S, N], in place)."""
+    if resid.dtype != _f32():
+        raise ValueError("resid: must be float32")
     p = make_proj_problem(y, w, resid, block, resid.shape[1])
+    _kept_check(kept_idx, n_kept, p.batch, resid.shape[1] // block)
+    if y.shape[1] < max_kept_blocks * block:
+        raise ValueError("y: fewer rows than max_kept_blocks * block")
     st = lib.jenga_proj_scatter_add(ctypes.byref(p), _ptr(y), _ptr(w), _ptr(kept_idx), _ptr(n_kept),
                                     int(max_kept_blocks), _ptr(resid), _stream(stream))
     _check("jenga_proj_scatter_add", st)
@@ -342,7 +444,12 @@ def proj_gather_scatter_add(a, w, kept_idx, n_kept, max_kept_blocks: int, block:
                             stream=None) -> None:
     """resid[b, pos(r)] += a[b, pos(r)] @ w^T at the kept rows (a bf16 [B, S, K] full rows,
     resid fp32 [B, S, N], in place)."""
+    if resid.dtype != _f32():
+        raise ValueError("resid: must be float32")
     p = make_proj_problem(a, w, resid, block, resid.shape[1])
+    _kept_check(kept_idx, n_kept, p.batch, resid.shape[1] // block)
+    if a.shape[1] != resid.shape[1]:
+        raise ValueError("a: one row per token of resid expected")
     st = lib.jenga_proj_gather_scatter_add(ctypes.byref(p), _ptr(a), _ptr(w), _ptr(kept_idx),
                                            _ptr(n_kept), int(max_kept_blocks), _ptr(resid),
                                            _stream(stream))
@@ -363,6 +470,9 @@ def mlp_act_scores(x, w1, w_up, kind: int, block: int, workspace=None, stream=No
     import torch
     B, S, _ = x.shape
     F = w1.shape[0]
+    if w_up is not None:
+        _dense("w_up", w_up, tuple(w1.shape), torch.bfloat16)
+    _ws_check(workspace)
     act = torch.empty((B, S, F), dtype=torch.bfloat16, device=x.device)
     tok = torch.empty((B, S), dtype=torch.float32, device=x.device)
     blk = torch.empty((B, S // block), dtype=torch.float32, device=x.device)
@@ -409,6 +519,12 @@ def lm_head_ce(h, w, wt, targets, n_segments: int = 1, workspace=None, stream=No
     import torch
     T, d = h.shape
     V = w.shape[0]
+    _dense("h", h, (T, d), torch.bfloat16)
+    _dense("w", w, (V, d), torch.bfloat16)
+    _dense("wt", wt, (d, V), torch.bfloat16)
+    _dense("targets", targets, (T,), torch.int32)
+    _ws_check(workspace)
+    _on_device(h=h, w=w, wt=wt, targets=targets, workspace=workspace)
     p = loss_problem(T, d, V, n_segments)
     ws = workspace if workspace is not None else alloc_workspace(loss_workspace_bytes(p), h.device)
     row_loss = torch.empty((T,), dtype=torch.float32, device=h.device)
