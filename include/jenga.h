@@ -92,7 +92,7 @@ size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks
  * and key block, the log2 of the block's partial sum; a memory-bound pass turns these into the
  * mass per key block.  The queries go through both passes in chunks (segment-based peak
  * cutting, [summary] 4.4.2), so the workspace holds the partial sums of one chunk only:
- * chunk * S/block floats per (batch, head), chunk = 128 * ceil(1024 / (B * Hq)) queries
+ * chunk * S/block floats per (batch, head), chunk = 128 * ceil(2048 / (B * Hq)) queries
  * (at most S rounded up to 128) -- linear in S.  fp32: two streamed passes (row log-sum-exp,
  * then received mass per key).  The result is deterministic: sums are fp64 and reduced in a
  * fixed order.

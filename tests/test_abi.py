@@ -170,21 +170,21 @@ def test_workspace_scales_with_segments_and_kept_blocks(J):
 def test_score_workspace(J):
     # lse2 rows (fp32) and mass slots (fp64, one per 32 keys), each rounded to 256 bytes; the
     # bf16 path adds the partial log2-sums of one query chunk: chunk * nKB floats per (batch,
-    # head), chunk = 128 * ceil(1024 / (B * Hq)) queries, at most S rounded up to 128
+    # head), chunk = 128 * ceil(2048 / (B * Hq)) queries, at most S rounded up to 128
     up = lambda x: (x + 255) // 256 * 256
     for B, S, Hq, block in ((1, 32768, 32, 128), (2, 4096, 8, 64), (1, 576, 2, 192),
                             (1, 131072, 32, 128), (1, 16384, 32, 64)):
         nkb = S // block
-        chunk = min(128 * -(-1024 // (B * Hq)), -(-S // 128) * 128)
+        chunk = min(128 * -(-2048 // (B * Hq)), -(-S // 128) * 128)
         base = up(B * Hq * S * 4) + up(B * Hq * (S // 32) * 8)
         p16 = _problem(J, B=B, S=S, Hq=Hq, Hkv=Hq, D=128, block=block, dtype=1)
         assert J.workspace_bytes(p16, J.JENGA_OP_SCORE) == base + up(B * Hq * nkb * chunk * 4)
         p32 = _problem(J, B=B, S=S, Hq=Hq, Hkv=Hq, D=64, block=block, dtype=0)
         assert J.workspace_bytes(p32, J.JENGA_OP_SCORE) == base
-    # 32K tokens, 32 heads, block 128: chunks of 4096 queries, 128 MiB of partial sums beside
+    # 32K tokens, 32 heads, block 128: chunks of 8192 queries, 256 MiB of partial sums beside
     # 4.25 MiB of rows and slots (the whole causal triangle would be 514 MiB)
     c5 = _problem(J, S=32768, Hq=32, Hkv=32, D=128, block=128, dtype=1)
-    assert J.workspace_bytes(c5, J.JENGA_OP_SCORE) == 4 * 2**20 + 2**18 + 128 * 2**20
+    assert J.workspace_bytes(c5, J.JENGA_OP_SCORE) == 4 * 2**20 + 2**18 + 256 * 2**20
     # linear in S: at four times the tokens the partial sums take four times the bytes
     c5x4 = _problem(J, S=131072, Hq=32, Hkv=32, D=128, block=128, dtype=1)
     rows = lambda S: S * 32 * 4 + S // 32 * 32 * 8

@@ -3,7 +3,7 @@
 - Selection over more than 1024 blocks: the selection workgroup compacts 1024 blocks per pass,
   so 1025, 4096 and 16384 blocks take two, four and sixteen passes.
 - Scoring in several query chunks: the bf16 scorer stores the partial log2-sums of one chunk
-  of 128 * ceil(1024 / (B * Hq)) queries at a time, so many heads and a few thousand tokens
+  of 128 * ceil(2048 / (B * Hq)) queries at a time, so many heads and a few thousand tokens
   already need more than one chunk (and a ragged last one).
 - Attention with more than 1024 kept blocks: the kernels resolve kept ranks through an LDS copy
   of the first 1024 kept-block indices and read the rest from the global list.
@@ -61,17 +61,17 @@ def test_select_past_1024_blocks(J):
 
 
 CHUNK_CASES = [
-    # B, S, Hq, Hkv, D, block: B*Hq = 128 -> chunks of 1024 queries: 1024 + 512
-    (2, 1536, 64, 8, 64, 64),
-    # B*Hq = 256 -> chunks of 512 queries: 512 + 512 + 256, block 128
-    (8, 1280, 32, 32, 128, 128),
+    # B, S, Hq, Hkv, D, block: B*Hq = 256 -> chunks of 1024 queries: 1024 + 512
+    (4, 1536, 64, 8, 64, 64),
+    # B*Hq = 512 -> chunks of 512 queries: 512 + 512 + 256, block 128
+    (16, 1280, 32, 32, 128, 128),
 ]
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,D,block", CHUNK_CASES)
 def test_scores_in_several_chunks(J, B, S, Hq, Hkv, D, block):
     import torch
-    chunk = 128 * -(-1024 // (B * Hq))
+    chunk = 128 * -(-2048 // (B * Hq))
     assert S > chunk                                   # the case really spans several chunks
     q, k, _, _, _ = random_inputs(B, S, Hq, Hkv, D, "bf16", seed=31 * S + Hq)
     say(f"chunked scores B{B} S{S} Hq{Hq} Hkv{Hkv} D{D} block{block} chunk{chunk}")

@@ -109,10 +109,12 @@ size_t score_eq2_ws_bytes(const jenga_problem* p) {
 
 // bf16 scoring runs in chunks of queries; each chunk's partial log2-sums (one per query and key
 // block) are turned into mass before the next chunk.  A chunk holds enough 128-query tiles for
-// at least 1024 workgroups (four per compute unit), or S rounded up to the tile if that is
-// less, so the stored partials are chunk x S/block floats per (batch, head): linear in S.
+// at least 2048 workgroups (two rounds of four per compute unit: the heaviest-first order then
+// pairs long tiles with short ones; one round lasts as long as its longest tile), or S rounded
+// up to the tile if that is less, so the stored partials are chunk x S/block floats per
+// (batch, head): linear in S.
 constexpr int kScoreTile = 128;
-constexpr int kScoreMinWorkgroups = 1024;
+constexpr int kScoreMinWorkgroups = 2048;
 
 int score_chunk(const jenga_problem* p) {
   const int64_t heads = (int64_t)p->batch * p->n_heads_q;
