@@ -33,6 +33,9 @@ KERNELS = ("k_slse64", "k_sblock_mass", "k_eq2_tiles", "k_eq2_reduce", "k_select
            "k_proj_logits", "k_ce_rows", "k_proj_dh", "k_mlp_act_gated", "k_mlp_block",
            "k_proj_gather_scatter")
 METRIC = "fwd+bwd token-sparse attn TFLOP/s (kept FLOPs) & tokens/s at S=32K; % MFMA peak"
+# MFMA work the backward kernel executes per (query head, causal kept pair), in units of D flop:
+# its dK/dV tiles form S, dP, dV and dK (8 D), its dQ tiles S, dP and dQ (6 D)
+BWD_EXECUTED_D = 14.0
 
 
 def parse():
@@ -274,13 +277,14 @@ def main():
     K = args.steps
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the timed steps carry only the per-layer phase events (6 per layer and step); the
+    # library's per-kernel events are off here and run in a separate pass below
+    J.timing_enable(False)
     torch.cuda.synchronize()
-    J.timing_enable(True)
     start.record(stream)
     for i in range(K):
         run_step(evs[i])
     end.record(stream)
-    J.timing_enable(False)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / K
@@ -301,11 +305,26 @@ def main():
     tflops = (fwd_flop + bwd_flop) / (attn_ms * 1e-3) / 1e12
     score_flop = 2.0 * D * Hq * B * L * S * (S + 1) / 2       # one q.k per causal pair and head
 
+    # Per-kernel times: the same K steps again, with the library's own HIP events around every
+    # launch (recorded on the stream each kernel runs on).  Kept out of the headline steps above
+    # so that the headline carries no per-launch instrumentation.
+    torch.cuda.synchronize()
+    J.timing_enable(True)
+    inst0, inst1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    inst0.record(stream)
+    for i in range(K):
+        run_step()
+    inst1.record(stream)
+    J.timing_enable(False)
+    torch.cuda.synchronize()
+    inst_ms_per_step = inst0.elapsed_time(inst1) / K
+    peak_steps = torch.cuda.max_memory_allocated()       # before any later section resets it
+
     # dominant attention kernel: k_bwd64 (one launch per backward segment, running the dK/dV
-    # and dQ tiles of the segment), timed by the library's own HIP events on the stream it runs
-    # on, over the timed steps above.  Its algorithmic work is seven 2*D contractions per (query
-    # head, causal kept pair): the dK/dV tiles recompute the scores and form dP, dV and dK; the
-    # dQ tiles recompute the scores and dP and form dQ.
+    # and dQ tiles of the segment).  Its algorithmic work, as the metric counts it, is the
+    # backward's five 2*D contractions per (query head, causal kept pair): 10*D.  What it
+    # executes is seven: the dK/dV tiles recompute the scores and form dP, dV and dK; the dQ
+    # tiles recompute the scores and dP and form dQ (14*D), reported beside it.
     kern_ms = {}
     for name in KERNELS:
         n, t = J.timing_query(name)
@@ -314,9 +333,11 @@ def main():
     n_bwd, t_bwd = kern_ms.get("k_bwd64", (0, 0.0))
     roofline = None
     if n_bwd:
-        bwd_flop_launch = 14.0 * D * Hq * pairs * K / n_bwd
+        bwd_flop_launch = 10.0 * D * Hq * pairs * K / n_bwd
+        exec_flop_launch = BWD_EXECUTED_D * D * Hq * pairs * K / n_bwd
         avg_ms = t_bwd / n_bwd
         achieved = bwd_flop_launch / (avg_ms * 1e-3) / 1e12
+        executed = exec_flop_launch / (avg_ms * 1e-3) / 1e12
         traffic = None
         tfile = os.path.join(ROOT, "profiles", f"traffic_k_bwd64_{args.config}.json")
         if os.path.exists(tfile) and args.kept == "selected" and nseg == cfg.n_segments:
@@ -328,7 +349,12 @@ def main():
                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                     "algorithmic_flop_per_launch": bwd_flop_launch, "launches": n_bwd,
-                    "avg_launch_us": round(avg_ms * 1e3, 2)}
+                    "avg_launch_us": round(avg_ms * 1e3, 2),
+                    "executed_flop_per_launch": exec_flop_launch,
+                    "executed_tflops": round(executed, 2),
+                    "executed_frac": round(executed / BF16_PEAK_TFLOPS, 4),
+                    "timed_in": "a separate instrumented pass of the same steps "
+                                f"({round(inst_ms_per_step, 3)} ms per step)"}
     kernel_avg_us = {kk: {"launches": n, "avg_us": round(1e3 * t / n, 2)} for kk, (n, t) in kern_ms.items()}
 
     # Eq. 2 literal scoring (the NEXT-row scoring mode), timed on its own after the steps: one
@@ -449,6 +475,16 @@ def main():
         loss_seg = {"tokens": T, "d_model": dm, "vocab": V}
         for nseg_l in (1, 8):
             pl = J.loss_problem(T, dm, V, nseg_l)
+            # transient: the allocator's peak during one call (the call allocates its workspace
+            # and outputs from torch) minus what stays allocated after it (the outputs)
+            torch.cuda.synchronize()
+            base_l = torch.cuda.memory_allocated()
+            torch.cuda.reset_peak_memory_stats()
+            outs_l = J.lm_head_ce(hh, wv, wvt, tg, nseg_l)
+            torch.cuda.synchronize()
+            transient_l = torch.cuda.max_memory_allocated() - torch.cuda.memory_allocated()
+            outputs_l = torch.cuda.memory_allocated() - base_l
+            del outs_l
             ws_l = J.alloc_workspace(J.loss_workspace_bytes(pl), dev)
             J.lm_head_ce(hh, wv, wvt, tg, nseg_l, ws_l)                  # warm-up
             torch.cuda.synchronize()
@@ -461,7 +497,8 @@ def main():
             ms = l0.elapsed_time(l1) / K
             loss_seg[f"segments_{nseg_l}"] = {
                 "ms": round(ms, 3), "tflops": round(4.0 * T * dm * V / (ms * 1e-3) / 1e12, 2),
-                "transient_mib": round(J.loss_workspace_bytes(pl) / 2**20, 1)}
+                "transient_mib": round(transient_l / 2**20, 1),
+                "outputs_mib": round(outputs_l / 2**20, 1)}
             del ws_l
         del hh, wv, wvt, tg
 
@@ -479,7 +516,7 @@ def main():
         copy_ms = c0.elapsed_time(c1)
         del a, bcopy
 
-    mem = {"max_allocated_gib": round(torch.cuda.max_memory_allocated() / 2**30, 2),
+    mem = {"max_allocated_gib": round(peak_steps / 2**30, 2),
            "saved_activations_mib_per_layer": round(
                (B * ncap * Hq * D * (2 if cfg.dtype == "bf16" else 4) + B * Hq * ncap * 4 + B * nkb * 4) / 2**20, 2),
            "fwd_workspace_mib": round(layers[0]["ws_f"].numel() / 2**20, 2),
@@ -533,24 +570,52 @@ def main():
                      "attn_ms_per_step": round(sc_ms, 3),
                      "tflops": round(14.0 * D * Hq * sc_pairs / (sc_ms * 1e-3) / 1e12, 2)}
 
-    # Memory at this workload's shapes, one layer, over keep ratios and segment counts: the
-    # activations the backward keeps (o_saved, lse, the kept list) and the backward's transient,
-    # which is exactly its workspace (the library allocates nothing else).
+    # Memory at this workload's shapes, one layer, over keep ratios and segment counts, measured
+    # with torch's allocator counters around the calls (every buffer comes from torch; the
+    # library allocates nothing): the forward's peak (saved activations + its workspace), the
+    # activations it leaves for the backward (o_saved, lse, the kept list), and the backward's
+    # transient peak.  Q/K/V, the residual and the gradients are caller-owned and excluded.
     memory_sweep = []
     if cfg.dtype == "bf16":
-        p0 = layers[0]["p"]
+        st0 = layers[0]
+        dq_m = torch.zeros_like(st0["dq"])
+        dk_m = torch.zeros_like(st0["dk"])
+        dv_m = torch.zeros_like(st0["dv"])
+        res_m = x0.clone()
+        mib = lambda x: round(x / 2**20, 2)
         for r in (0.125, 0.25, 0.5, 0.75, 1.0):
             kk = J.topk_count(r, nkb)
+            kb_np = np.full((B, nkb), -1, np.int32)
+            kb_np[:, :kk] = random_kept_blocks(nkb, kk, 7000 + kk)
             for nn in (1, 8):
+                torch.cuda.synchronize()
+                base = torch.cuda.memory_allocated()
+                torch.cuda.reset_peak_memory_stats()
+                kept_m = torch.from_numpy(kb_np).to(dev)
+                nk_m = torch.full((B,), kk, dtype=torch.int32, device=dev)
+                o_m, lse_m = J.sparse_attn_fwd(st0["q"], st0["k"], st0["v"], kept_m, nk_m, kk, blk, res_m)
+                torch.cuda.synchronize()
+                fwd_peak = torch.cuda.max_memory_allocated() - base
+                saved = torch.cuda.memory_allocated() - base
+                torch.cuda.reset_peak_memory_stats()
+                base2 = torch.cuda.memory_allocated()
+                J.sparse_attn_bwd(st0["q"], st0["k"], st0["v"], kept_m, nk_m, kk, blk, o_m, lse_m, dout,
+                                  n_segments=nn, grads=(dq_m, dk_m, dv_m))
+                torch.cuda.synchronize()
+                bwd_peak = torch.cuda.max_memory_allocated() - base2
                 memory_sweep.append({
                     "keep": r, "n_segments": nn, "kept_tokens": B * kk * blk,
-                    "saved_activation_mib": round((B * kk * blk * Hq * (es * D + 4) + B * nkb * 4) / 2**20, 2),
-                    "bwd_transient_mib": round(J.workspace_bytes(p0, J.JENGA_OP_BWD, kk, nn) / 2**20, 2)})
+                    "fwd_peak_mib": mib(fwd_peak), "saved_activation_mib": mib(saved),
+                    "bwd_transient_mib": mib(bwd_peak)})
+                del kept_m, nk_m, o_m, lse_m
+        del dq_m, dk_m, dv_m, res_m
 
     # ---------------- CPU baseline: the oracle on a bounded sample of the same workload ----
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, sample_np)
+        sel_mode = {"topk": 0, "thresh_rel": 1}[cfg.select_mode]
+        cpu = cpu_baseline(cfg, sample_np, layers[0]["scores"].cpu().numpy(),
+                           (sel_mode, cfg.select_param, cfg.force_first))
 
     out = {
         "metric": METRIC,
@@ -598,41 +663,113 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, sample, budget_s: float = 12.0):
-    """Oracle fwd+bwd (float64 NumPy, as written) on a bounded sample of the workload: layer 0,
-    kept blocks 0..k-1 (a self-contained causal prefix of the literal top-k set's size), one
-    query head at a time until about budget_s seconds of CPU work have been spent."""
+def host_facts():
+    """The host the oracle baseline ran on: logical CPUs, the CPUs this process may use,
+    physical cores and model (lscpu), and the BLAS thread count NumPy's BLAS runs with."""
+    import subprocess
+    facts = {"os_cpu_count": os.cpu_count()}
+    try:
+        facts["usable_cpus"] = len(os.sched_getaffinity(0))
+    except Exception:
+        pass
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        kv = {}
+        for line in out.splitlines():
+            if ":" in line:
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+        facts["cpu_model"] = kv.get("Model name")
+        if kv.get("Core(s) per socket") and kv.get("Socket(s)"):
+            facts["physical_cores"] = int(kv["Core(s) per socket"]) * int(kv["Socket(s)"])
+        if kv.get("Thread(s) per core"):
+            facts["threads_per_core"] = int(kv["Thread(s) per core"])
+    except Exception:
+        pass
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"] + [0])
+    except Exception:
+        pass
+    facts["blas_threads"] = threads or None
+    facts["omp_num_threads"] = os.environ.get("OMP_NUM_THREADS")
+    return facts
+
+
+def cpu_baseline(cfg, sample, scores0, select_args, budget_s: float = 12.0, score_budget_s: float = 5.0):
+    """The oracle as written (float64 NumPy, BLAS threaded over the host cores) timed per op on
+    bounded samples of this workload's layer 0:
+      score:  block scores of a causal prefix of min(S, 4096) tokens, one query head after
+              another for about score_budget_s seconds;
+      select: the selection rule on the GPU's scores of layer 0 (all blocks);
+      fwd, bwd: attention forward and backward over kept blocks 0..k-1 (a self-contained causal
+              prefix of the literal top-k set's size), one query head after another until
+              about budget_s seconds have been spent.
+    `value` is fwd+bwd TFLOP/s on the metric's kept-FLOP count."""
     import oracle
     from synth.generate import to_bf16_bits_f32
     q_all, k_all, v_all, dout_all = sample
+    host = host_facts()
+    bf = (lambda a: to_bf16_bits_f32(a)) if cfg.dtype == "bf16" else (lambda a: a)
+    G = cfg.n_heads_q // cfg.n_heads_kv
+    kv_of = lambda h: min(h // G, k_all.shape[2] - 1)
+    prep = lambda a, S_s, i: np.ascontiguousarray(a[:, :S_s, i:i + 1])
+    D, B = cfg.head_dim, cfg.batch
+
+    # score
+    S_sc = min(cfg.seq_len, 4096)
+    hs, t_sc = 0, 0.0
+    while hs < q_all.shape[2] and t_sc < score_budget_s:
+        q, k = bf(prep(q_all, S_sc, hs)), bf(prep(k_all, S_sc, kv_of(hs)))
+        t0 = time.time()
+        oracle.block_scores(q, k, cfg.block)
+        t_sc += time.time() - t0
+        hs += 1
+    score_flop = 2.0 * D * hs * B * S_sc * (S_sc + 1) / 2
+
+    # select
+    mode, param, ff = select_args
+    reps, t0 = 0, time.time()
+    while reps < 20 or time.time() - t0 < 0.2:
+        for b in range(scores0.shape[0]):
+            oracle.select_blocks(scores0[b], mode, param, ff)
+        reps += 1
+    t_sel = (time.time() - t0) / reps
+
+    # fwd, bwd
     nb = min(cfg.n_blocks, 128)
     S_s = nb * cfg.block
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 0) for i in threadpool_info()] + [0]) or os.cpu_count()
-    except Exception:
-        threads = os.cpu_count()
     kept = np.arange(nb)
-    heads, dt = 0, 0.0
-    while heads < q_all.shape[2] and dt < budget_s:
+    heads, t_f, t_b = 0, 0.0, 0.0
+    while heads < q_all.shape[2] and t_f + t_b < budget_s:
         h = heads
-        g = 0 if cfg.n_heads_kv != cfg.n_heads_q else h
-        prep = lambda a, i: np.ascontiguousarray(a[:, :S_s, i:i + 1])
-        q, k, v = prep(q_all, h), prep(k_all, g), prep(v_all, g)
-        if cfg.dtype == "bf16":
-            q, k, v = to_bf16_bits_f32(q), to_bf16_bits_f32(k), to_bf16_bits_f32(v)
-        dout = prep(dout_all, h)
+        q, k, v = bf(prep(q_all, S_s, h)), bf(prep(k_all, S_s, kv_of(h))), bf(prep(v_all, S_s, kv_of(h)))
+        dout = prep(dout_all, S_s, h)
         t0 = time.time()
         oracle.attn_fwd_compact(q, k, v, kept, cfg.block)
+        t1 = time.time()
         oracle.attn_bwd_compact(q, k, v, kept, cfg.block, dout)
-        dt += time.time() - t0
+        t2 = time.time()
+        t_f += t1 - t0
+        t_b += t2 - t1
         heads += 1
-    Nk = S_s
-    flop = 14.0 * cfg.head_dim * heads * cfg.batch * Nk * (Nk + 1) / 2
-    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"layer 0, query heads 0..{heads - 1}, kept blocks 0..{nb - 1} ({Nk} kept "
-                      f"tokens, a self-contained causal prefix), attention fwd+bwd in float64 NumPy"}
+    pairs = B * S_s * (S_s + 1) / 2
+    fwd_flop, bwd_flop = 4.0 * D * heads * pairs, 10.0 * D * heads * pairs
+    return {"value": round((fwd_flop + bwd_flop) / (t_f + t_b) / 1e12, 5), "unit": "TFLOP/s",
+            "cores": int(host.get("blas_threads") or host.get("usable_cpus") or os.cpu_count()),
+            "kind": "oracle", "seconds": round(t_sc + t_f + t_b + t_sel * reps, 2),
+            "sample": f"layer 0; fwd+bwd: query heads 0..{heads - 1}, kept blocks 0..{nb - 1} ({S_s} kept "
+                      f"tokens, a self-contained causal prefix), float64 NumPy",
+            "per_op": {
+                "score": {"seconds": round(t_sc, 3), "gflops": round(score_flop / t_sc / 1e9, 3),
+                          "sample": f"query heads 0..{hs - 1}, causal prefix of {S_sc} tokens",
+                          "work": "2*D flop per causal (query, key) pair and head"},
+                "select": {"us_per_call": round(1e6 * t_sel, 1), "n_blocks": int(scores0.shape[1]),
+                           "batch_rows": int(scores0.shape[0])},
+                "fwd": {"seconds": round(t_f, 3), "gflops": round(fwd_flop / t_f / 1e9, 3)},
+                "bwd": {"seconds": round(t_b, 3), "gflops": round(bwd_flop / t_b / 1e9, 3)}},
+            "host": host}
 
 
 if __name__ == "__main__":
