@@ -40,7 +40,8 @@ typedef enum {
   JENGA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive size, bad stride or alignment */
   JENGA_ERR_UNSUPPORTED = -2,  /* valid but unsupported shape (head_dim, block, dtype)      */
   JENGA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than jenga_workspace_bytes   */
-  JENGA_ERR_LAUNCH = -4        /* a kernel launch failed                                    */
+  JENGA_ERR_LAUNCH = -4,       /* a kernel launch failed                                    */
+  JENGA_ERR_SCRATCH_LIMIT = -5 /* needs more than the no-alloc entry point's fixed scratch  */
 } jenga_status;
 
 typedef enum {
@@ -209,6 +210,32 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
                                     const float* dout, float* dq, float* dk, float* dv,
                                     int n_segments, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * jenga_sparse_attn_bwd_segmented_noalloc — jenga_sparse_attn_bwd_segmented for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It takes no workspace argument and allocates nothing: its scratch is
+ * a fixed device array of JENGA_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU,
+ * located on the first call on each device and held until the process ends.  The caller
+ * still passes every input and output, with the meanings, layouts and results of
+ * jenga_sparse_attn_bwd_segmented (the same kernels run).
+ *
+ * Returns JENGA_ERR_SCRATCH_LIMIT, launching nothing, when
+ * jenga_workspace_bytes(p, JENGA_OP_BWD, max_kept_blocks, n_segments) exceeds
+ * JENGA_NOALLOC_SCRATCH_BYTES; the backward's scratch shrinks as 1/n_segments, so a larger
+ * n_segments makes a bigger problem fit (32K tokens x 32 heads x 128, half the blocks kept:
+ * 8 segments need 48.5 MiB).  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (different streams, or host threads) race and must be ordered
+ * by the caller.  The scratch keeps the last call's contents; nothing in it needs to start
+ * at zero.
+ */
+#define JENGA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int jenga_sparse_attn_bwd_segmented_noalloc(const jenga_problem* p, const void* q, const void* k,
+                                            const void* v, const int32_t* kept_idx,
+                                            const int32_t* n_kept, int max_kept_blocks,
+                                            const void* o_saved, const float* lse,
+                                            const float* dout, float* dq, float* dk, float* dv,
+                                            int n_segments, void* stream);
 
 /*
  * Permutation-free token movement around the projections ([notes] §4.4; [summary] 4.4.1: the

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(J):
 
 
 def test_status_strings(J):
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert J.status_string(st) != "unknown status"
     assert J.status_string(7) == "unknown status"
 
@@ -335,3 +335,20 @@ def test_binding_refuses_views_dtypes_and_shapes(J):
     with pytest.raises(ValueError, match="targets: dtype"):
         J.lm_head_ce(torch.zeros((64, 128), dtype=torch.bfloat16), torch.zeros((256, 128), dtype=torch.bfloat16),
                      torch.zeros((128, 256), dtype=torch.bfloat16), torch.zeros(64, dtype=torch.int64))
+
+
+def test_noalloc_backward_refuses_past_its_scratch(J):
+    # 32K tokens x 32 heads x 128 with 128 kept blocks of 128: one segment needs 388 MiB of
+    # scratch, past the fixed 64 MiB, so the call returns JENGA_ERR_SCRATCH_LIMIT before
+    # anything is launched; eight segments would need 48.5 MiB (within the limit)
+    p = _problem(J, S=32768, Hq=32, Hkv=32, D=128, block=128, dtype=1)
+    assert J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 1) > J.NOALLOC_SCRATCH_BYTES
+    assert J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 8) <= J.NOALLOC_SCRATCH_BYTES
+    st = J.lib.jenga_sparse_attn_bwd_segmented_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 128,
+                                                       FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None)
+    assert st == J.JENGA_ERR_SCRATCH_LIMIT
+    assert "n_segments" in J.status_string(st)
+    # argument checks come first, as in the entry point with a workspace
+    assert J.lib.jenga_sparse_attn_bwd_segmented_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                                                         FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                                                         None) == J.JENGA_ERR_INVALID_ARG

@@ -18,6 +18,8 @@ JENGA_ERR_INVALID_ARG = -1
 JENGA_ERR_UNSUPPORTED = -2
 JENGA_ERR_WORKSPACE = -3
 JENGA_ERR_LAUNCH = -4
+JENGA_ERR_SCRATCH_LIMIT = -5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 JENGA_DTYPE_F32 = 0
 JENGA_DTYPE_BF16 = 1
 JENGA_SELECT_TOPK = 0
@@ -33,7 +35,8 @@ JENGA_OP_SCORE_EQ2 = 3
 
 EXPORTED = ["jenga_status_string", "jenga_topk_count", "jenga_workspace_bytes",
             "jenga_score_blocks", "jenga_score_blocks_eq2", "jenga_select_blocks",
-            "jenga_sparse_attn_fwd", "jenga_sparse_attn_bwd_segmented", "jenga_proj_gather",
+            "jenga_sparse_attn_fwd", "jenga_sparse_attn_bwd_segmented",
+            "jenga_sparse_attn_bwd_segmented_noalloc", "jenga_proj_gather",
             "jenga_proj_scatter_add", "jenga_proj_gather_scatter_add", "jenga_mlp_workspace_bytes",
             "jenga_mlp_act_scores", "jenga_loss_workspace_bytes", "jenga_lm_head_ce_segmented",
             "jenga_timing_enable", "jenga_timing_query"]
@@ -89,6 +92,9 @@ def _load() -> ctypes.CDLL:
     lib.jenga_sparse_attn_bwd_segmented.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                                                     vp, i32, vp, sz, vp]
     lib.jenga_sparse_attn_bwd_segmented.restype = i32
+    lib.jenga_sparse_attn_bwd_segmented_noalloc.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                                            vp, vp, vp, i32, vp]
+    lib.jenga_sparse_attn_bwd_segmented_noalloc.restype = i32
     PP = ctypes.POINTER(JengaProjProblem)
     lib.jenga_proj_gather.argtypes = [PP, vp, vp, vp, vp, i32, vp, vp]
     lib.jenga_proj_gather.restype = i32
@@ -312,6 +318,30 @@ def jenga_sparse_attn_bwd_segmented(p: JengaProblem, q, k, v, kept_idx, n_kept,
         int(n_segments), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check("jenga_sparse_attn_bwd_segmented", st)
+
+
+def jenga_sparse_attn_bwd_segmented_noalloc(p: JengaProblem, q, k, v, kept_idx, n_kept,
+                                            max_kept_blocks: int, o_saved, lse, dout, dq, dk, dv,
+                                            n_segments: int, stream=None) -> None:
+    """The segmented backward with the library's fixed per-GPU scratch instead of a workspace
+    (no allocation anywhere; calls on one GPU must not overlap)."""
+    B, S, Hq, D, Hkv = p.batch, p.seq_len, p.n_heads_q, p.head_dim, p.n_heads_kv
+    ncap = int(max_kept_blocks) * p.block
+    _dense("kept_idx", kept_idx, (B, _nkb(p)), _i32())
+    _dense("n_kept", n_kept, (B,), _i32())
+    _dense("o_saved", o_saved, (B, ncap, Hq, D), q.dtype)
+    _dense("lse", lse, (B, Hq, ncap), _f32())
+    _dense("dout", dout, (B, S, Hq, D), _f32())
+    _dense("dq", dq, (B, S, Hq, D), _f32())
+    _dense("dk", dk, (B, S, Hkv, D), _f32())
+    _dense("dv", dv, (B, S, Hkv, D), _f32())
+    _on_device(q=q, k=k, v=v, kept_idx=kept_idx, n_kept=n_kept, o_saved=o_saved, lse=lse,
+               dout=dout, dq=dq, dk=dk, dv=dv)
+    st = lib.jenga_sparse_attn_bwd_segmented_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_idx), _ptr(n_kept),
+        int(max_kept_blocks), _ptr(o_saved), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        int(n_segments), _stream(stream))
+    _check("jenga_sparse_attn_bwd_segmented_noalloc", st)
 
 
 # ------------------------------------------------------------------------------------------

@@ -2,6 +2,7 @@
 // launch geometry and the segment loop.  Every check happens before the first launch.
 #include <math.h>
 #include <algorithm>
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -17,6 +18,31 @@ constexpr size_t kAlign = 256;
 constexpr double kOffsetLimit = 4294967296.0;   // 32-bit buffer-resource offsets
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Scratch of jenga_sparse_attn_bwd_segmented_noalloc: a fixed device array, one copy per GPU,
+// held until the process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in for the symbol): each GPU's copy is located once, with that GPU
+// current, through hipGetSymbolAddress, and that pointer is what the kernels receive.
+constexpr size_t kNoAllocScratchBytes = JENGA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) static unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return JENGA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return JENGA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return JENGA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return JENGA_OK;
+}
 
 int check_problem(const jenga_problem* p, bool need_qkv_strides) {
   if (!p) return JENGA_ERR_INVALID_ARG;
@@ -243,6 +269,9 @@ const char* jenga_status_string(int status) {
     case JENGA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case JENGA_ERR_WORKSPACE: return "workspace missing or too small";
     case JENGA_ERR_LAUNCH: return "kernel launch failed";
+    case JENGA_ERR_SCRATCH_LIMIT:
+      return "the problem needs more scratch than the no-alloc entry point's fixed buffer holds "
+             "(raise n_segments: the backward's scratch shrinks as 1/n_segments)";
     default: return "unknown status";
   }
 }
@@ -411,12 +440,17 @@ int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, 
   return JENGA_OK;
 }
 
-int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const void* k,
-                                    const void* v, const int32_t* kept_idx, const int32_t* n_kept,
-                                    int max_kept_blocks, const void* o_saved, const float* lse,
-                                    const float* dout, float* dq, float* dk, float* dv,
-                                    int n_segments, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The segmented backward behind both entry points.  With noalloc set, the workspace is this
+// GPU's fixed scratch array, fetched only after every argument check has passed.
+int bwd_segmented(const jenga_problem* p, const void* q, const void* k, const void* v,
+                  const int32_t* kept_idx, const int32_t* n_kept, int max_kept_blocks,
+                  const void* o_saved, const float* lse, const float* dout, float* dq, float* dk,
+                  float* dv, int n_segments, void* workspace, size_t workspace_bytes, bool noalloc,
+                  void* stream) {
   int st = check_problem(p, true);
   if (st != JENGA_OK) return st;
   const int nkb = p->seq_len / p->block;
@@ -428,6 +462,12 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
   const int ncap = max_kept_blocks * p->block;
   if (n_segments < 1 || n_segments > ncap / 64) return JENGA_ERR_INVALID_ARG;
   const size_t need = bwd_ws_bytes(p, max_kept_blocks, n_segments);
+  if (noalloc) {
+    if (need > kNoAllocScratchBytes) return JENGA_ERR_SCRATCH_LIMIT;
+    const int st2 = scratch_of_current_device(&workspace);
+    if (st2 != JENGA_OK) return st2;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
     return JENGA_ERR_WORKSPACE;
   const int L = seg_len_of(ncap, n_segments);
@@ -472,6 +512,30 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
     if (e != hipSuccess) return JENGA_ERR_LAUNCH;
   }
   return JENGA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const void* k,
+                                    const void* v, const int32_t* kept_idx, const int32_t* n_kept,
+                                    int max_kept_blocks, const void* o_saved, const float* lse,
+                                    const float* dout, float* dq, float* dk, float* dv,
+                                    int n_segments, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return bwd_segmented(p, q, k, v, kept_idx, n_kept, max_kept_blocks, o_saved, lse, dout, dq, dk,
+                       dv, n_segments, workspace, workspace_bytes, false, stream);
+}
+
+int jenga_sparse_attn_bwd_segmented_noalloc(const jenga_problem* p, const void* q, const void* k,
+                                            const void* v, const int32_t* kept_idx,
+                                            const int32_t* n_kept, int max_kept_blocks,
+                                            const void* o_saved, const float* lse,
+                                            const float* dout, float* dq, float* dk, float* dv,
+                                            int n_segments, void* stream) {
+  return bwd_segmented(p, q, k, v, kept_idx, n_kept, max_kept_blocks, o_saved, lse, dout, dq, dk,
+                       dv, n_segments, nullptr, 0, true, stream);
 }
 
 
