@@ -96,20 +96,44 @@ def _short(name: str) -> str:
 
 
 def summarize(trace_dir, fetch_dir, write_dir, bench_log, cfg_name="c5"):
-    """Write profiles/kernels_<cfg>.md (rocprofv3 kernel-trace stats next to the bench's own
-    HIP-event averages) and profiles/traffic_k_bwd64_<cfg>.json (HBM bytes per launch from
-    FETCH_SIZE / WRITE_SIZE, each scaled by the ratio known bytes / counter of the calibration
-    copy, which moves exactly 1 GiB each way)."""
+    """Write profiles/kernels_<cfg>.md (per-kernel times from the rocprofv3 kernel trace next to
+    the bench's own HIP-event averages, and HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE)
+    and profiles/traffic_k_bwd64_<cfg>.json.  Only the dispatches of the bench's steps count:
+    the first (warmup + 2 * steps) * (launches per step) dispatches of each kernel in issue
+    order (warm-up, timed and instrumented passes); later sections of the bench (memory sweep,
+    scattered kept sets, NEXT rows) launch the same kernels at other sizes.  Counter bytes are
+    scaled by the ratio known bytes / counter of the calibration copy, which moves exactly 1 GiB
+    each way."""
     import csv
     with open(bench_log) as f:
         line = [x for x in f if x.startswith("{")][-1]
     bench = json.loads(line)
-    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    K, W = bench["steps"], bench["warmup"]
+    ev = bench.get("kernel_avg_us", {})
+    per_step = {k: v["launches"] // K for k, v in ev.items()}       # instrumented pass: K steps
+    budget = {k: (W + 2 * K) * n for k, n in per_step.items()}
+
+    def first_n(rows, key, name_of):
+        seen, out = {}, []
+        for r in sorted(rows, key=key):
+            k = name_of(r)
+            if k in budget:
+                seen[k] = seen.get(k, 0) + 1
+                if seen[k] > budget[k]:
+                    continue
+            out.append((k, r))
+        return out
+
+    trace = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    dur = {}
+    for k, r in first_n(trace, lambda r: int(r["Start_Timestamp"]), lambda r: _short(r["Kernel_Name"])):
+        n, t = dur.get(k, (0, 0.0))
+        dur[k] = (n + 1, t + (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
 
     def counters(d):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
         agg = {}
-        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
-            k = _short(r["Kernel_Name"])
+        for k, r in first_n(rows, lambda r: int(r["Dispatch_Id"]), lambda r: _short(r["Kernel_Name"])):
             n, t = agg.get(k, (0, 0.0))
             agg[k] = (n + 1, t + float(r["Counter_Value"]) * 1024.0)
         return agg
@@ -117,44 +141,39 @@ def summarize(trace_dir, fetch_dir, write_dir, bench_log, cfg_name="c5"):
     cal = "calibration copy (elementwise neg, 1 GiB)"
     f_fac = 2**30 / (fetch[cal][1] / fetch[cal][0])
     w_fac = 2**30 / (write[cal][1] / write[cal][0])
-    lines = [f"# Kernel times, {cfg_name} bench step (rocprofv3 kernel trace)", "",
-             "Command (repository root on the GPU host):", "",
-             "    cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-             "-d <repo>/gpurun_out/prof_trace -o run -- python3 <repo>/bench.py --steps 2 --warmup 1 "
-             "--no-cpu-baseline", "",
-             f"Kernel source hash {kernel_source_hash()} (code of the kernel sources, comments and "
-             "layout excluded).  Columns: rocprofv3 calls / average / total "
-             "over warmup + timed steps; the bench's own HIP-event average over the timed steps.", "",
-             "| kernel | calls | rocprof avg us | rocprof total ms | % | bench event avg us |",
+    lines = [f"# Kernel times and HBM bytes, {cfg_name} bench step (rocprofv3)", "",
+             "Commands (repository root on the GPU host; `cd /tmp && export TMPDIR=/tmp` first):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/prof_trace -o run "
+             "-- python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline > <repo>/gpurun_out/prof_trace.log",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/prof_fetch -o run -- "
+             "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
+             "    rocprofv3 --pmc WRITE_SIZE ... (same, -d <repo>/gpurun_out/prof_write)",
+             "    python3 bench.py --summarize gpurun_out/prof_trace gpurun_out/prof_fetch gpurun_out/prof_write "
+             "gpurun_out/prof_trace.log", "",
+             f"Kernel source hash {kernel_source_hash()} (code of the attention kernel sources, comments and "
+             "layout excluded).  Only the dispatches of the bench's steps are counted: per kernel, the first "
+             "(warmup + 2 x steps) x (launches per step) dispatches in issue order (warm-up, timed and "
+             "instrumented passes of the same step); the bench's later sections (memory sweep, scattered "
+             "kept sets, NEXT rows) are left out.", "",
+             f"Calibration: the 1 GiB copy reads FETCH_SIZE {fetch[cal][1] / fetch[cal][0] / 2**20:.1f} MiB and "
+             f"WRITE_SIZE {write[cal][1] / write[cal][0] / 2**20:.1f} MiB, so counter bytes are scaled by "
+             f"{f_fac:.3f} (fetch) and {w_fac:.3f} (write).", "",
+             "| kernel | dispatches | rocprof avg us | bench event avg us | fetch MiB/dispatch | write MiB/dispatch |",
              "|---|---|---|---|---|---|"]
-    ev = bench.get("kernel_avg_us", {})
-    for r in rows:
-        k = _short(r["Name"])
-        e = ev.get(k, {}).get("avg_us", "")
-        lines.append(f"| {k} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                     f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.2f} | {e} |")
-    lines += ["", "HBM counters (separate rocprofv3 --pmc runs of the same bench with --copy-calibration, "
-              "--steps 1 --warmup 1):", "",
-              "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/prof_fetch -o run -- "
-              "python3 <repo>/bench.py --steps 1 --warmup 1 --no-cpu-baseline --copy-calibration",
-              "    rocprofv3 --pmc WRITE_SIZE ... (same, -d <repo>/gpurun_out/prof_write)", "",
-              f"Calibration: the 1 GiB copy reads FETCH_SIZE {fetch[cal][1] / fetch[cal][0] / 2**20:.1f} MiB and "
-              f"WRITE_SIZE {write[cal][1] / write[cal][0] / 2**20:.1f} MiB, so counter bytes are scaled by "
-              f"{f_fac:.3f} (fetch) and {w_fac:.3f} (write).", "",
-              "| kernel | dispatches | fetch MiB/dispatch (scaled) | write MiB/dispatch (scaled) |",
-              "|---|---|---|---|"]
-    for k in sorted(fetch):
-        if k == cal or k not in write:
+    for k in sorted(dur, key=lambda k: -dur[k][1]):
+        if k not in budget:
             continue
-        n = fetch[k][0]
-        lines.append(f"| {k} | {n} | {fetch[k][1] / n * f_fac / 2**20:.1f} | "
-                     f"{write[k][1] / write[k][0] * w_fac / 2**20:.1f} |")
+        n, t = dur[k]
+        e = ev.get(k, {}).get("avg_us", "")
+        fm = f"{fetch[k][1] / fetch[k][0] * f_fac / 2**20:.1f}" if k in fetch else ""
+        wm = f"{write[k][1] / write[k][0] * w_fac / 2**20:.1f}" if k in write else ""
+        lines.append(f"| {k} | {n} | {t / n:.1f} | {e} | {fm} | {wm} |")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"kernels_{cfg_name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     k = "k_bwd64"
     t = {"kernel": k, "config": cfg_name, "kernel_source_hash": kernel_source_hash(),
-         "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4),
+         "dispatches": fetch[k][0], "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4),
          "fetch_bytes_per_launch": round(fetch[k][1] / fetch[k][0] * f_fac),
          "write_bytes_per_launch": round(write[k][1] / write[k][0] * w_fac)}
     t["hbm_bytes_per_launch"] = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
