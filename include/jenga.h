@@ -12,11 +12,15 @@
  *     be strided views (strides in elements for batch, token and head); every other tensor
  *     is dense as stated at its argument.
  *   - All pointers are device pointers unless stated otherwise; the caller owns and frees
- *     every buffer, including the workspace.  The library allocates nothing and keeps no
- *     state between calls, so calls on different streams may run concurrently as long as
- *     they do not share output buffers.
- *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues work and
- *     returns; there is no host synchronisation.  The kept-block count stays on the device.
+ *     every buffer, including the workspace.  The library allocates nothing.  Apart from the
+ *     per-GPU scratch array of jenga_sparse_attn_bwd_segmented_noalloc and the optional
+ *     per-kernel timing records it keeps no state between calls, so calls on different
+ *     streams may run concurrently as long as they do not share output buffers.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues kernels on
+ *     it and returns: no memset, copy or host synchronisation.  The kept-block count stays on
+ *     the device.  A sequence of calls can therefore be captured in a HIP graph and replayed
+ *     (jenga_sparse_attn_bwd_segmented_noalloc must first have run once on the device, which
+ *     places its scratch array; per-kernel timing must be off during capture).
  *   - Errors: every argument check happens before anything is launched; a negative status
  *     means nothing was enqueued.  JENGA_ERR_LAUNCH reports a failed launch (from
  *     hipGetLastError).  Faults inside a kernel surface at the caller's next synchronisation.
