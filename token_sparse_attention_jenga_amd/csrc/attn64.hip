@@ -98,7 +98,7 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
   __shared__ __attribute__((aligned(1024))) char sC[STAGE];
   __shared__ int ktab[kKeptTab];
 
-  const Tile3 tl = xcd_tile();
+  const Tile3 tl = xcd_tile_weight_major();
   const int b = tl.z, h = tl.y;
   const int g = h / (p.Hq / p.Hkv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;

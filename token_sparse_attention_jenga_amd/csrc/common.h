@@ -155,6 +155,44 @@ __device__ inline Tile3 xcd_tile() {
   return {L % nx, (L / nx) % ny, L / (nx * ny)};
 }
 
+// The same ranges, visited weight-major in groups, for grids whose tiles get lighter along x
+// (causal row tiles numbered heaviest first).  When XCD x's range holds whole rows (y, z) of
+// tiles, its workgroups take tiles 0..G-1 of every row of the range, then tiles G..2G-1 of every
+// row, and so on (G = kWeightMajorGroup; the last group may be shorter).  Row by row, the heavy
+// tiles of the range's later rows went out after the light tiles of its first rows and the
+// launch ended on them; tile by tile across the rows, the XCD swept several rows' K at once and
+// fetched twice the bytes from beyond its L2.  Groups of 32 tiles keep most of the balance and
+// the fetch of the row-by-row order.  Otherwise (ranges that split a row) the order of
+// xcd_tile().
+constexpr int kWeightMajorGroup = 32;
+
+__device__ inline Tile3 xcd_tile_weight_major() {
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int nwg = nx * ny * (int)gridDim.z;
+  const int lin = (int)blockIdx.x + nx * ((int)blockIdx.y + ny * (int)blockIdx.z);
+  const int q = nwg >> 3, r = nwg & 7, xcd = lin & 7, slot = lin >> 3;
+  int L;
+  if (r == 0 && q % nx == 0) {
+    const int rows = q / nx;                             // whole rows per XCD range
+    const int G = min(kWeightMajorGroup, nx);
+    const int nfull = nx / G, full_slots = nfull * rows * G;
+    int row, t;
+    if (slot < full_slots) {                             // a group of G tiles of every row
+      const int grp = slot / (rows * G), in = slot - grp * rows * G;
+      row = in / G;
+      t = grp * G + (in - row * G);
+    } else {                                             // the last, shorter group
+      const int P = nx - nfull * G, in = slot - full_slots;
+      row = in / P;
+      t = nfull * G + (in - row * P);
+    }
+    L = (xcd * rows + row) * nx + t;
+  } else {
+    L = xcd * q + min(xcd, r) + slot;
+  }
+  return {L % nx, (L / nx) % ny, L / (nx * ny)};
+}
+
 // The same XCD-contiguous ranges for a GEMM grid (x = row tiles, y = column tiles), with the
 // tiles of a range visited in groups of GM row tiles: within a group the row tile runs fastest,
 // so the workgroups an XCD runs side by side cover GM row panels and a few column panels, and

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
   __shared__ __attribute__((aligned(1024))) char sB[C::NAT32];
   __shared__ __attribute__((aligned(1024))) char sC[C::NAT32];
 
-  const Tile3 tl = xcd_tile();
+  const Tile3 tl = xcd_tile_weight_major();
   const int b = tl.z, h = tl.y;
   const int g = h / (p.Hq / p.Hkv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, lc = l & 31;
