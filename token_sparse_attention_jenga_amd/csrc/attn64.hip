@@ -11,9 +11,10 @@
 // forward, Q and dO in the dK/dV tiles), or, in the dQ tiles, two transposing 8-byte reads of
 // the natural K tile (see tiles64.h).
 //
-//   k_pack_tp   kept rows of V / Q (head h) -> TP tiles [D][32] in a workspace
+//   k_pack_tp   kept rows of V (head h) -> TP tiles [D][32] in a workspace (forward)
 //   k_fwd64     forward:   S^T = K Q^T, online softmax per query (lane-local), O^T += V^T P^T
-//   k_prep64    backward prologue per segment: D_i = dO_i.O_i, dOut -> bf16 natural + TP
+//   k_prep64    backward prologue per segment: D_i = dO_i.O_i, dOut -> bf16 natural + TP,
+//               the segment's Q rows -> TP
 //   k_bwd64     one launch per segment with two kinds of workgroup tiles (no atomics):
 //                 dK/dV, key-major:   S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q
 //                 dQ, query-major:    S^T = K Q^T, dP^T = V dO^T, dQ += dS K
@@ -35,6 +36,25 @@ struct PackArgs {
 };
 
 // ------------------------------------------------------------------------------------------
+// Write a 32-row natural tile staged in LDS (row pitch D + 8 elements) as its TP tile [D][32]
+// at dst; the 256 threads of the workgroup write 16 bytes each per pass.
+template <int D>
+__device__ __forceinline__ void write_tp_tile(const bf16* tile, char* dst) {
+  constexpr int PITCH = D + 8;
+  for (int idx = threadIdx.x; idx < D * 4; idx += 256) {
+    const int d = idx >> 2, c = idx & 3;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(uint16_t, tile[pi16(8 * c + e) * PITCH + d]);
+    u32x4 wv;
+    wv[0] = v[0] | ((uint32_t)v[1] << 16);
+    wv[1] = v[2] | ((uint32_t)v[3] << 16);
+    wv[2] = v[4] | ((uint32_t)v[5] << 16);
+    wv[3] = v[6] | ((uint32_t)v[7] << 16);
+    *(u32x4*)(dst + d * 64 + c * 16) = wv;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_pack_tp(PackArgs a) {
   constexpr int PITCH = D + 8;                        // elements; breaks bank aliasing
@@ -53,19 +73,7 @@ __global__ __launch_bounds__(256) void k_pack_tp(PackArgs a) {
     *(u32x4*)(tile + row * PITCH + c * 8) = ld16(src + (int64_t)(pos0 + row) * a.s1 + c * 8);
   }
   __syncthreads();
-  char* dst = (char*)a.dst + ((((int64_t)b * a.H + h) * a.tiles_per_head + t) * D) * 64;
-  for (int idx = tid; idx < D * 4; idx += 256) {
-    const int d = idx >> 2, c = idx & 3;
-    uint16_t v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(uint16_t, tile[pi16(8 * c + e) * PITCH + d]);
-    u32x4 wv;
-    wv[0] = v[0] | ((uint32_t)v[1] << 16);
-    wv[1] = v[2] | ((uint32_t)v[3] << 16);
-    wv[2] = v[4] | ((uint32_t)v[5] << 16);
-    wv[3] = v[6] | ((uint32_t)v[7] << 16);
-    *(u32x4*)(dst + d * 64 + c * 16) = wv;
-  }
+  write_tp_tile<D>(tile, (char*)a.dst + ((((int64_t)b * a.H + h) * a.tiles_per_head + t) * D) * 64);
 }
 
 template <int D>
@@ -277,13 +285,17 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
 }
 
 // ------------------------------------------------------------------------------------------
-// Backward prologue (one segment): D_i, dOut -> bf16 natural rows and TP tiles
+// Backward prologue (one segment): D_i, dOut -> bf16 natural rows and TP tiles, and the TP
+// tiles of the same ranks' Q rows (one launch: each workgroup holds 32 ranks of one head)
 // ------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_prep64(BwdParams p) {
   constexpr int E = D / 8;                    // elements per thread (8 threads per row)
   constexpr int PITCH = D + 8;
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int QC = 32 * CPR / 256;          // Q chunks per thread
   __shared__ bf16 tile[32 * PITCH];
+  __shared__ bf16 qtile[32 * PITCH];
   const int b = blockIdx.z, h = blockIdx.y, t = blockIdx.x, tid = threadIdx.x;
   const int32_t* kept = p.kept + (int64_t)b * p.nkb;
   const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
@@ -292,6 +304,14 @@ __global__ __launch_bounds__(256) void k_prep64(BwdParams p) {
   const int r0 = qs + 32 * t;
   if (r0 >= qe) return;                       // qe - qs is a multiple of 64
   const int pos0 = rank_to_pos(kept, p.block, r0);
+  // the Q rows' loads go out first; they land while dO . O is formed
+  const bf16* qsrc = (const bf16*)p.q + b * p.qs[0] + h * p.qs[2];
+  u32x4 qv[QC];
+#pragma unroll
+  for (int i = 0; i < QC; ++i) {
+    const int idx = tid + 256 * i, qr = idx / CPR, c = idx % CPR;
+    qv[i] = ld16(qsrc + (int64_t)(pos0 + qr) * p.qs[1] + c * 8);
+  }
   const int row = tid >> 3, part = tid & 7;
   const float* drow = p.dout + (((int64_t)b * p.S + pos0 + row) * p.Hq + h) * D + part * E;
   const char* orow = (const char*)p.o_saved + ((((int64_t)b * p.ncap + r0 + row) * p.Hq + h) * D + part * E) * 2;
@@ -325,20 +345,15 @@ __global__ __launch_bounds__(256) void k_prep64(BwdParams p) {
     *(u32x4*)(wrow + c * 16) = v;
     *(u32x4*)(tile + row * PITCH + part * E + c * 8) = v;
   }
-  __syncthreads();
-  char* dst = (char*)p.dotp + ((((int64_t)b * p.Hq + h) * (p.seg_len / 32) + (r0 - qs) / 32) * D) * 64;
-  for (int idx = tid; idx < D * 4; idx += 256) {
-    const int d = idx >> 2, c = idx & 3;
-    uint16_t v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(uint16_t, tile[pi16(8 * c + e) * PITCH + d]);
-    u32x4 wv;
-    wv[0] = v[0] | ((uint32_t)v[1] << 16);
-    wv[1] = v[2] | ((uint32_t)v[3] << 16);
-    wv[2] = v[4] | ((uint32_t)v[5] << 16);
-    wv[3] = v[6] | ((uint32_t)v[7] << 16);
-    *(u32x4*)(dst + d * 64 + c * 16) = wv;
+  for (int i = 0; i < QC; ++i) {
+    const int idx = tid + 256 * i, qr = idx / CPR, c = idx % CPR;
+    *(u32x4*)(qtile + qr * PITCH + c * 8) = qv[i];
   }
+  __syncthreads();
+  const int64_t tp_tile = ((int64_t)b * p.Hq + h) * (p.seg_len / 32) + (r0 - qs) / 32;
+  write_tp_tile<D>(tile, (char*)p.dotp + tp_tile * D * 64);
+  write_tp_tile<D>(qtile, (char*)p.qtp + tp_tile * D * 64);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -828,10 +843,6 @@ static hipError_t bwd64_segment_t(const BwdParams& p, hipStream_t st) {
     k_prep64<D><<<dim3((seg_cap + 31) / 32, p.Hq, p.B), 256, 0, st>>>(p);
     e = hipGetLastError();
   }
-  if (e != hipSuccess) return e;
-  PackArgs a{p.q, p.qs[0], p.qs[1], p.qs[2], p.kept, p.n_kept, p.block, p.nkb, p.max_kept_blocks,
-             p.seg * L, seg_cap, L / 32, p.Hq, p.qtp};
-  e = pack_tp<D>(a, p.B, st);
   if (e != hipSuccess) return e;
   const int seg_end = p.seg * L + seg_cap;
   constexpr int KG = 32 * DKDV_NW, QG = 32 * DQ_NB * DQ_NW;
