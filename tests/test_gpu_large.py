@@ -7,6 +7,8 @@
   already need more than one chunk (and a ragged last one).
 - Attention with more than 1024 kept blocks: the kernels resolve kept ranks through an LDS copy
   of the first 1024 kept-block indices and read the rest from the global list.
+- Tile dispatch with several (batch, head) rows per XCD range in groups with a shorter last
+  group, for two batch rows of different kept counts.
 """
 import numpy as np
 import pytest
@@ -126,3 +128,49 @@ def test_attention_past_1024_kept_blocks(J):
     assert max_abs(dq.cpu().numpy()[0, pos[qr], 0], rdq[0]) <= BF16_TOL
     for g in (dq, dk, dv):
         assert np.all(g.cpu().numpy()[0, elim] == 0.0)
+
+
+def test_weight_major_dispatch_two_batch_rows(J):
+    """Two batch rows, 8 query heads, 80 kept blocks of 64 in one row and 72 in the other: the
+    forward's XCD ranges then hold two (batch, head) rows each, visited in groups of 32 tiles with
+    a shorter last group (40 tiles of 128 queries per row); the backward's light launches send
+    their dK/dV tiles out weight-major.  Sampled rows of both batch rows against the oracle,
+    eliminated rows bitwise unchanged."""
+    import torch
+    B, S, Hq, Hkv, D, block = 2, 8192, 8, 2, 128, 64
+    nkb = S // block
+    rng = np.random.default_rng(4040)
+    kept = [np.sort(rng.choice(nkb, 80, replace=False)).astype(np.int64),
+            np.sort(rng.choice(nkb, 72, replace=False)).astype(np.int64)]
+    q, k, v, x0, dout = random_inputs(B, S, Hq, Hkv, D, "bf16", seed=4041)
+    kt, nk = kept_tensor(kept, nkb)
+    maxk = 80
+    say(f"weight-major dispatch: B{B} S{S} Hq{Hq} Hkv{Hkv} kept 80/72 blocks of {block}, 3 segments")
+    qd, kd, vd = to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16")
+    resid = torch.from_numpy(x0.copy()).cuda()
+    o_saved, lse = J.sparse_attn_fwd(qd, kd, vd, kt, nk, maxk, block, resid)
+    dq, dk, dv = J.sparse_attn_bwd(qd, kd, vd, kt, nk, maxk, block, o_saved, lse,
+                                   torch.from_numpy(dout).cuda(), n_segments=3)
+    torch.cuda.synchronize()
+    r = resid.cpu().numpy()
+    for b in range(B):
+        Nk = len(kept[b]) * block
+        pos = oracle.token_positions(kept[b], block)
+        ranks = np.unique(np.concatenate([np.arange(0, 8), rng.choice(Nk, 24, replace=False),
+                                          np.arange(Nk - 8, Nk)]))
+        for h in (0, 5):
+            O, LSE = oracle.attn_fwd_rows(q, k, v, kept[b], block, b, h, ranks)
+            assert max_abs(r[b, pos[ranks], h] - x0[b, pos[ranks], h], O) <= BF16_TOL, (b, h)
+            assert max_abs(o_saved.float().cpu().numpy()[b, ranks, h], O) <= BF16_TOL, (b, h)
+        elim = np.setdiff1d(np.arange(S), pos)
+        assert np.array_equal(r[b, elim], x0[b, elim])
+        # keys late in the kept order (a key needs every later query row), queries anywhere
+        kr = np.unique(np.concatenate([np.arange(Nk - 6, Nk), Nk // 2 + rng.choice(Nk // 2, 4, replace=False)]))
+        qr = np.unique(np.concatenate([rng.choice(Nk, 6, replace=False), np.arange(Nk - 4, Nk)]))
+        for g in (0, 1):
+            rdk, rdv, rdq = oracle.attn_bwd_sampled(q, k, v, kept[b], block, dout, b, g, kr, qr)
+            assert max_abs(dk.cpu().numpy()[b, pos[kr], g], rdk) <= BF16_TOL, (b, g)
+            assert max_abs(dv.cpu().numpy()[b, pos[kr], g], rdv) <= BF16_TOL, (b, g)
+            G = Hq // Hkv
+            for i, hh in enumerate(range(g * G, (g + 1) * G)):
+                assert max_abs(dq.cpu().numpy()[b, pos[qr], hh], rdq[i]) <= BF16_TOL, (b, g, hh)
