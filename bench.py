@@ -142,14 +142,15 @@ def summarize(trace_dir, fetch_dir, write_dir, bench_log, cfg_name="c5"):
     f_fac = 2**30 / (fetch[cal][1] / fetch[cal][0])
     w_fac = 2**30 / (write[cal][1] / write[cal][0])
     lines = [f"# Kernel times and HBM bytes, {cfg_name} bench step (rocprofv3)", "",
-             "Commands (repository root on the GPU host; `cd /tmp && export TMPDIR=/tmp` first):", "",
-             "    rocprofv3 --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/prof_trace -o run "
-             "-- python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline > <repo>/gpurun_out/prof_trace.log",
-             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/prof_fetch -o run -- "
+             "Commands (`<repo>` the repository root, `<out>` any output directory; "
+             "`cd /tmp && export TMPDIR=/tmp` first):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_trace -o run "
+             "-- python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline > <out>/prof_trace.log",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/prof_fetch -o run -- "
              "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
-             "    rocprofv3 --pmc WRITE_SIZE ... (same, -d <repo>/gpurun_out/prof_write)",
-             "    python3 bench.py --summarize gpurun_out/prof_trace gpurun_out/prof_fetch gpurun_out/prof_write "
-             "gpurun_out/prof_trace.log", "",
+             "    rocprofv3 --pmc WRITE_SIZE ... (same, -d <out>/prof_write)",
+             "    python3 bench.py --summarize <out>/prof_trace <out>/prof_fetch <out>/prof_write "
+             "<out>/prof_trace.log", "",
              f"Kernel source hash {kernel_source_hash()} (code of the attention kernel sources, comments and "
              "layout excluded).  Only the dispatches of the bench's steps are counted: per kernel, the first "
              "(warmup + 2 x steps) x (launches per step) dispatches in issue order (warm-up, timed and "
