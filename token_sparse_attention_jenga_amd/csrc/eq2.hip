@@ -13,7 +13,8 @@
 //                 diagonal block and the block maximum, times c / Hq (c > 0 factors out of the
 //                 positive part and the maximum).  Q and K tiles load in 64-column chunks of
 //                 head_dim; the next chunk loads into a second LDS buffer while the current one
-//                 is multiplied.
+//                 is multiplied.  A head's positive part is added while the next head's
+//                 products run.
 //   k_eq2_reduce  s_n = sum over m >= n in a fixed order (fp64), rounded once to fp32.
 #include "common.h"
 #include "kernels.h"
@@ -59,6 +60,57 @@ __device__ inline bool pair_of(int t, int nkb, int& m, int& n) {
   return m < nkb && n <= m;
 }
 
+// max(x, 0) as one integer max on the bits: a float with the sign bit set is a negative int32
+// (-0 included), any other a non-negative one, so this gives x for x > 0 and +0 otherwise.
+// (fmaxf first quietens an operand that comes out of an MFMA, one more VALU instruction per
+// element: 4.9 against 5.3 ms per 32K-token layer.)
+__device__ inline float pos_part(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
+// One 64-column head_dim chunk of a wave's HB x HB sub-tiles: W += Q K^T over the chunk's k-steps
+// (from zero on a head's first chunk), with the positive part of sub-tiles [R0, R1) of the
+// previous head's scores R added to acc between the MFMAs, so that the VALU work of one head
+// runs under the MFMA work of the next within the wave.  The operand reads run two k-steps
+// ahead.
+template <int HB, int R0, int R1, bool FIRST>
+__device__ __attribute__((always_inline)) inline void eq2_chunk(const char* Q0, const char* K0,
+                                                                const int* nat, f32x16* W,
+                                                                const f32x16* R, f32x16* acc) {
+  using C = T64<64>;
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s) {
+    bf16x8 a[HB], bk[HB];
+#pragma unroll
+    for (int i = 0; i < HB; ++i) a[i] = ldo(Q0 + i * C::NAT32, nat[s]);
+#pragma unroll
+    for (int i = 0; i < HB; ++i) bk[i] = ldo(K0 + i * C::NAT32, nat[s]);
+#pragma unroll
+    for (int i = 0; i < HB; ++i)
+#pragma unroll
+      for (int j = 0; j < HB; ++j)
+        W[HB * i + j] = Mfma<bf16>::mma(a[i], bk[j], (FIRST && s == 0) ? zero16() : W[HB * i + j]);
+  }
+#pragma unroll
+  for (int t = R0; t < R1; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] += pos_part(R[t][r]);
+  // reads of k-steps 0 and 1; then per k-step s its MFMAs, each followed by its share of the
+  // VALU work, and the reads of step s + 2
+  constexpr int MF = C::NS * HB * HB, VPM = 2 * 16 * (R1 - R0) / MF;
+  static_assert(VPM * MF == 2 * 16 * (R1 - R0), "VALU work spreads evenly over the MFMAs");
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 * HB, 0);
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s) {
+#pragma unroll
+    for (int m = 0; m < HB * HB; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (VPM > 0) __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+    }
+    if (s + 2 < C::NS) __builtin_amdgcn_sched_group_barrier(0x100, 2 * HB, 0);
+  }
+}
+
 template <int D, int BLK>
 __global__ __launch_bounds__(256, 2) void k_eq2_tiles(Eq2Params p) {
   // Tiles are staged in 64-column chunks of head_dim (the scores of a head are summed over its
@@ -102,49 +154,60 @@ __global__ __launch_bounds__(256, 2) void k_eq2_tiles(Eq2Params p) {
     }
   };
 
-  f32x16 acc[SPW], sc[SPW];
-#pragma unroll
-  for (int t = 0; t < SPW; ++t) acc[t] = sc[t] = zero16();
-  // sub-tile t of this wave: query sub-block qsb(t), key sub-block ksb(t).  The waves take the
-  // four quadrants of the SB x SB sub-tiles, so a wave's SB/2 query and SB/2 key operand reads
-  // of a k-step serve (SB/2)^2 MFMAs
+  // sub-tile t = HB i + j of this wave: query sub-block qsb0 + i, key sub-block ksb0 + j.  The
+  // waves take the four quadrants of the SB x SB sub-tiles, so a wave's HB query and HB key
+  // operand reads of a k-step serve HB^2 MFMAs
   constexpr int HB = SB / 2;
   static_assert(HB * HB == SPW, "one quadrant of sub-tiles per wave");
-  auto qsb = [&](int t) { return (w >> 1) * HB + t / HB; };
-  auto ksb = [&](int t) { return (w & 1) * HB + t % HB; };
+  const int qsb0 = (w >> 1) * HB, ksb0 = (w & 1) * HB;
 
-  auto compute = [&](int u, const char* buf) {
+  // Heads in pairs: head 2i's products go to sx, head 2i+1's to sy; chunk c of a head adds the
+  // positive part of sub-tiles [c SPW / DC, (c + 1) SPW / DC) of the previous head.  Before the
+  // first head the array read holds zeros, which add nothing.
+  f32x16 acc[SPW], sx[SPW], sy[SPW];
 #pragma unroll
-    for (int t = 0; t < SPW; ++t) {
-      const char* Qt = buf + qsb(t) * C::NAT32;
-      const char* Kt = buf + (SB + ksb(t)) * C::NAT32;
-#pragma unroll
-      for (int s = 0; s < C::NS; ++s) sc[t] = Mfma<bf16>::mma(ldo(Qt, rp.nat[s]), ldo(Kt, rp.nat[s]), sc[t]);
-    }
-    if (u % DC == DC - 1) {                               // a head's scores are complete
-#pragma unroll
-      for (int t = 0; t < SPW; ++t) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] += fmaxf(sc[t][r], 0.f);
-        sc[t] = zero16();
-      }
-    }
-  };
+  for (int t = 0; t < SPW; ++t) acc[t] = sx[t] = sy[t] = zero16();
 
   issue(0, sA);
   wait_all_mem();
   __syncthreads();
-  for (int u = 0; u < nu; u += 2) {
-    if (u + 1 < nu) issue(u + 1, sB);
-    compute(u, sA);
-    wait_all_mem();
-    stage_barrier();
-    if (u + 1 >= nu) break;
-    if (u + 2 < nu) issue(u + 2, sA);
-    compute(u + 1, sB);
-    wait_all_mem();
-    stage_barrier();
+  // chunk c of head h: stage u = h DC + c, in buffer u % 2; stage u + 1 loads meanwhile
+#define EQ2_CHUNK(W, R, c, cur, nxt)                                                               \
+  do {                                                                                           \
+    const int u_ = h * DC + (c);                                                                 \
+    if (u_ + 1 < nu) issue(u_ + 1, nxt);                                                         \
+    eq2_chunk<HB, (c) * SPW / DC, ((c) + 1) * SPW / DC, (c) == 0>(                               \
+        cur + qsb0 * C::NAT32, cur + (SB + ksb0) * C::NAT32, rp.nat, W, R, acc);                \
+    wait_all_mem();                                                                              \
+    stage_barrier();                                                                             \
+  } while (0)
+  static_assert(DC == 1 || DC == 2, "head_dim 64 or 128");
+  // (one loop with the exit between the two heads of a pair: with a loop over pairs and the
+  // last head of an odd count after it, the compiler spilled 68 registers)
+  for (int h = 0;; ++h) {
+    // stage h DC + c sits in buffer (h DC + c) % 2
+    if constexpr (DC == 1) {
+      EQ2_CHUNK(sx, sy, 0, sA, sB);
+      if (++h >= p.Hq) break;
+      EQ2_CHUNK(sy, sx, 0, sB, sA);
+    } else {
+      EQ2_CHUNK(sx, sy, 0, sA, sB);
+      EQ2_CHUNK(sx, sy, 1, sB, sA);
+      if (++h >= p.Hq) break;
+      EQ2_CHUNK(sy, sx, 0, sA, sB);
+      EQ2_CHUNK(sy, sx, 1, sB, sA);
+    }
+    if (h + 1 >= p.Hq) break;
   }
+#undef EQ2_CHUNK
+  // the positive part of the last head
+  const bool last_in_x = p.Hq % 2 != 0;
+#pragma unroll
+  for (int t = 0; t < SPW; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] += pos_part(last_in_x ? sx[t][r] : sy[t][r]);
+  auto qsb = [&](int t) { return qsb0 + t / HB; };
+  auto ksb = [&](int t) { return ksb0 + t % HB; };
 
   // lane = key n*BLK + 32 ksb + lc; register r = query m*BLK + 32 qsb + 8(r/4) + 4hl + r%4.
   // Every e >= 0, so a masked element set to 0 cannot raise the maximum.
