@@ -169,6 +169,25 @@ def summarize(trace_dir, fetch_dir, write_dir, bench_log, cfg_name="c5"):
         fm = f"{fetch[k][1] / fetch[k][0] * f_fac / 2**20:.1f}" if k in fetch else ""
         wm = f"{write[k][1] / write[k][0] * w_fac / 2**20:.1f}" if k in write else ""
         lines.append(f"| {k} | {n} | {t / n:.1f} | {e} | {fm} | {wm} |")
+    # Eq. 2 scoring (a NEXT row) runs in a section of its own, once per layer at the workload's
+    # size, so every dispatch of its kernels counts
+    eq = bench.get("eq2_scoring") or {}
+    import re
+    shape = dict(re.findall(r"(\w+)=(\d+)", bench.get("config", {}).get("workload", "")))
+    one_size = [k for k in ("k_eq2_tiles", "k_eq2_reduce") if k in dur]
+    if one_size:
+        qk = int(shape.get("B", 0)) * int(shape.get("S", 0)) * (int(shape.get("Hq", 0)) + int(shape.get("Hkv", 0))) \
+            * int(shape.get("D", 0)) * 2
+        lines += ["", "Eq. 2 scoring, every dispatch of the bench's Eq. 2 section (one call per layer at the "
+                  f"workload's size; Q and K hold {qk / 2**20:.0f} MiB per layer):", "",
+                  "| kernel | dispatches | rocprof avg us | bench event avg us | fetch MiB/dispatch | write MiB/dispatch |",
+                  "|---|---|---|---|---|---|"]
+        for k in one_size:
+            n, t = dur[k]
+            e = eq.get("k_eq2_tiles_avg_us", "") if k == "k_eq2_tiles" else ""
+            fm = f"{fetch[k][1] / fetch[k][0] * f_fac / 2**20:.1f}" if k in fetch else ""
+            wm = f"{write[k][1] / write[k][0] * w_fac / 2**20:.1f}" if k in write else ""
+            lines.append(f"| {k} | {n} | {t / n:.1f} | {e} | {fm} | {wm} |")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"kernels_{cfg_name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -623,10 +642,18 @@ def main():
                                   n_segments=nn, grads=(dq_m, dk_m, dv_m))
                 torch.cuda.synchronize()
                 bwd_peak = torch.cuda.max_memory_allocated() - base2
+                # the same backward with one set of segment buffers (each prologue a launch of
+                # its own): the least transient the backward runs with
+                torch.cuda.reset_peak_memory_stats()
+                base3 = torch.cuda.memory_allocated()
+                J.sparse_attn_bwd(st0["q"], st0["k"], st0["v"], kept_m, nk_m, kk, blk, o_m, lse_m, dout,
+                                  n_segments=nn, grads=(dq_m, dk_m, dv_m), min_workspace=True)
+                torch.cuda.synchronize()
+                bwd_peak_min = torch.cuda.max_memory_allocated() - base3
                 memory_sweep.append({
                     "keep": r, "n_segments": nn, "kept_tokens": B * kk * blk,
                     "fwd_peak_mib": mib(fwd_peak), "saved_activation_mib": mib(saved),
-                    "bwd_transient_mib": mib(bwd_peak)})
+                    "bwd_transient_mib": mib(bwd_peak), "bwd_transient_min_mib": mib(bwd_peak_min)})
                 del kept_m, nk_m, o_m, lse_m
         del dq_m, dk_m, dv_m, res_m
 

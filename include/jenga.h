@@ -56,7 +56,13 @@ typedef enum {
 
 #define JENGA_FORCE_FIRST_BLOCK 1u  /* flag: block 0 is always kept */
 
-typedef enum { JENGA_OP_SCORE = 0, JENGA_OP_FWD = 1, JENGA_OP_BWD = 2, JENGA_OP_SCORE_EQ2 = 3 } jenga_op;
+typedef enum {
+  JENGA_OP_SCORE = 0,
+  JENGA_OP_FWD = 1,
+  JENGA_OP_BWD = 2,      /* the backward's workspace for its fastest schedule                  */
+  JENGA_OP_SCORE_EQ2 = 3,
+  JENGA_OP_BWD_MIN = 4   /* the least workspace the backward accepts (one segment's buffers)   */
+} jenga_op;
 
 /* Problem shape, shared by every call of one layer. */
 typedef struct jenga_problem {
@@ -80,9 +86,9 @@ const char* jenga_status_string(int status);
  * [1, n_blocks] (r widened to double).  Host-side; returns -1 if n_blocks < 1. */
 int jenga_topk_count(float keep_ratio, int n_blocks);
 
-/* Workspace bytes needed by `op` (JENGA_OP_SCORE, _FWD or _BWD) for this problem.
- * max_kept_blocks matters for _FWD and _BWD, n_segments for _BWD.  Returns 0 for an
- * invalid problem (and for ops that need no workspace). */
+/* Workspace bytes needed by `op` (a jenga_op) for this problem.  max_kept_blocks matters for
+ * _FWD and _BWD*, n_segments for _BWD*.  Returns 0 for an invalid problem (and for ops that
+ * need no workspace). */
 size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks, int n_segments);
 
 /*
@@ -188,8 +194,8 @@ int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, 
 /*
  * jenga_sparse_attn_bwd_segmented — backward of jenga_sparse_attn_fwd, computed over
  * n_segments contiguous ranges of kept query ranks one after the other so that the
- * transient buffers (the per-query dot(dO, O) terms and the operand copy of dOut) scale
- * with the segment, not the sequence ([notes] 4.4 segment-based peak cutting: process
+ * transient buffers (the per-query dot(dO, O) terms and the operand copies of dOut and Q)
+ * scale with the segment, not the sequence ([notes] 4.4 segment-based peak cutting: process
  * segments independently, aggregate their gradients, discard each segment's activations).
  *
  * With P the forward's probabilities and dO_i = dout[b][i][h] for i in T_k:
@@ -204,7 +210,12 @@ int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, 
  *   dq                [B][S][Hq][D] fp32, dense, accumulated (+=) at kept rows only
  *   dk, dv            [B][S][Hkv][D] fp32, dense, accumulated (+=) at kept rows only
  *   n_segments        1 <= n_segments <= max_kept_blocks*block/64
- *   workspace         >= jenga_workspace_bytes(p, JENGA_OP_BWD, max_kept_blocks, n_segments)
+ *   workspace         >= jenga_workspace_bytes(p, JENGA_OP_BWD_MIN, max_kept_blocks, n_segments)
+ *                     bytes, 256-byte aligned.  bf16 with two or more segments: a workspace of
+ *                     jenga_workspace_bytes(p, JENGA_OP_BWD, ...) = twice that holds two sets
+ *                     of segment buffers, and each segment's launch then also runs the next
+ *                     segment's prologue; with less, every prologue is a launch of its own.
+ *                     Both schedules give the same bits.
  * bf16: every gradient is accumulated by a fixed schedule, so results repeat bit for bit.
  * fp32: dq receives fp32 atomic additions, so its low bits may differ run to run.
  */
@@ -225,10 +236,11 @@ int jenga_sparse_attn_bwd_segmented(const jenga_problem* p, const void* q, const
  * jenga_sparse_attn_bwd_segmented (the same kernels run).
  *
  * Returns JENGA_ERR_SCRATCH_LIMIT, launching nothing, when
- * jenga_workspace_bytes(p, JENGA_OP_BWD, max_kept_blocks, n_segments) exceeds
+ * jenga_workspace_bytes(p, JENGA_OP_BWD_MIN, max_kept_blocks, n_segments) exceeds
  * JENGA_NOALLOC_SCRATCH_BYTES; the backward's scratch shrinks as 1/n_segments, so a larger
  * n_segments makes a bigger problem fit (32K tokens x 32 heads x 128, half the blocks kept:
- * 8 segments need 48.5 MiB).  Every call on one GPU shares that GPU's scratch: calls that
+ * 8 segments need 48.5 MiB).  When the scratch holds JENGA_OP_BWD's two sets of segment
+ * buffers, the faster schedule runs.  Every call on one GPU shares that GPU's scratch: calls that
  * overlap in time on one GPU (different streams, or host threads) race and must be ordered
  * by the caller.  The scratch keeps the last call's contents; nothing in it needs to start
  * at zero.

@@ -156,13 +156,19 @@ def test_fwd_bwd_validation(J):
 def test_workspace_scales_with_segments_and_kept_blocks(J):
     p = _problem(J, S=32768, Hq=32, Hkv=32, D=128, block=128, dtype=1)
     w1 = J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 1)
-    w8 = J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 8)
-    w8_half = J.workspace_bytes(p, J.JENGA_OP_BWD, 64, 8)
+    w8 = J.workspace_bytes(p, J.JENGA_OP_BWD_MIN, 128, 8)
+    w8_half = J.workspace_bytes(p, J.JENGA_OP_BWD_MIN, 64, 8)
     vtp = 32 * 128 * 128 * 128 * 2                # forward: transposed V tiles of all kept keys
     seg = lambda L: 2 * 32 * L * 4 + 3 * 32 * L * 128 * 2   # D, lse2, dOut, dOut^T and Q^T tiles
-    assert w1 == seg(16384)
+    assert w1 == seg(16384)                       # one segment: one set of buffers either way
+    assert J.workspace_bytes(p, J.JENGA_OP_BWD_MIN, 128, 1) == w1
     assert w8 == seg(2048)                        # the backward workspace shrinks as 1/N
     assert abs(w8_half * 2 - w8) <= 4096          # and scales with the kept tokens
+    # bf16 with two or more segments: the faster schedule takes two sets of segment buffers
+    assert J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 8) == 2 * w8
+    assert J.workspace_bytes(p, J.JENGA_OP_BWD, 64, 8) == 2 * w8_half
+    p32 = _problem(J, S=4096, Hq=4, Hkv=4, D=64, block=64, dtype=0)
+    assert J.workspace_bytes(p32, J.JENGA_OP_BWD, 32, 4) == J.workspace_bytes(p32, J.JENGA_OP_BWD_MIN, 32, 4)
     assert J.workspace_bytes(p, J.JENGA_OP_FWD, 128) == vtp
     assert J.workspace_bytes(_problem(J), J.JENGA_OP_FWD, 8) == 0       # fp32 path needs none
 
@@ -340,10 +346,12 @@ def test_binding_refuses_views_dtypes_and_shapes(J):
 def test_noalloc_backward_refuses_past_its_scratch(J):
     # 32K tokens x 32 heads x 128 with 128 kept blocks of 128: one segment needs 388 MiB of
     # scratch, past the fixed 64 MiB, so the call returns JENGA_ERR_SCRATCH_LIMIT before
-    # anything is launched; eight segments would need 48.5 MiB (within the limit)
+    # anything is launched; eight segments need 48.5 MiB (within the limit; their two-set
+    # schedule, 97 MiB, is not, so that call runs each prologue as a launch of its own)
     p = _problem(J, S=32768, Hq=32, Hkv=32, D=128, block=128, dtype=1)
-    assert J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 1) > J.NOALLOC_SCRATCH_BYTES
-    assert J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 8) <= J.NOALLOC_SCRATCH_BYTES
+    assert J.workspace_bytes(p, J.JENGA_OP_BWD_MIN, 128, 1) > J.NOALLOC_SCRATCH_BYTES
+    assert J.workspace_bytes(p, J.JENGA_OP_BWD_MIN, 128, 8) <= J.NOALLOC_SCRATCH_BYTES
+    assert J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 8) > J.NOALLOC_SCRATCH_BYTES
     st = J.lib.jenga_sparse_attn_bwd_segmented_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 128,
                                                        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None)
     assert st == J.JENGA_ERR_SCRATCH_LIMIT

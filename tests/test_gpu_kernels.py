@@ -185,6 +185,80 @@ def test_bwd_segments_equivalent(J):
         assert max_abs(a, b) <= 1e-5 * scale
 
 
+# B, S, Hq, Hkv, D, block, kept blocks per batch row, max_kept_blocks, segments
+SCHED_CASES = [
+    (2, 4096, 4, 2, 128, 64, (40, 26), 40, 3),   # short last segment; row 1 ends in segment 1
+    (1, 2048, 3, 1, 64, 128, (16,), 16, 4),       # grouped-query attention, head_dim 64
+    (1, 1024, 1, 1, 128, 64, (8,), 8, 8),         # two prologue groups per segment: a workgroup
+]                                                 # of the fused launch with idle halves
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,block,counts,maxk,nseg", SCHED_CASES)
+def test_bwd_schedules_bitwise(J, B, S, Hq, Hkv, D, block, counts, maxk, nseg):
+    """bf16 backward with two sets of segment buffers (each segment's launch also runs the next
+    segment's prologue) and with one set (each prologue a launch of its own): the same bits, and
+    within tolerance of the oracle."""
+    import torch
+    nkb = S // block
+    rng = np.random.default_rng(S + nseg)
+    kept = [np.sort(rng.choice(nkb, c, replace=False)) for c in counts]
+    q, k, v, x0, dout = random_inputs(B, S, Hq, Hkv, D, "bf16", seed=S + 3 * nseg)
+    qd, kd, vd = to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16")
+    kept_d, nk_d = kept_tensor(kept, nkb)
+    resid = torch.from_numpy(x0.copy()).cuda()
+    say(f"backward schedules B{B} S{S} Hq{Hq} Hkv{Hkv} D{D} block{block} kept {counts} N={nseg}")
+    o_saved, lse = J.sparse_attn_fwd(qd, kd, vd, kept_d, nk_d, maxk, block, resid)
+    dd = torch.from_numpy(dout).cuda()
+    p = J.make_problem(qd, kd, vd, block)
+    one = J.workspace_bytes(p, J.JENGA_OP_BWD_MIN, maxk, nseg)
+    assert J.workspace_bytes(p, J.JENGA_OP_BWD, maxk, nseg) == 2 * one
+    got = [J.sparse_attn_bwd(qd, kd, vd, kept_d, nk_d, maxk, block, o_saved, lse, dd, n_segments=nseg,
+                             min_workspace=lean) for lean in (False, True)]
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got[0], got[1]):
+        assert torch.equal(a, b), name
+    rq, rk, rv = oracle.attn_bwd(q, k, v, kept, block, dout)
+    tol = tol_for("bf16")
+    for b in range(B):
+        pos = oracle.token_positions(kept[b], block)
+        for name, g, ref in (("dq", got[0][0], rq), ("dk", got[0][1], rk), ("dv", got[0][2], rv)):
+            err = max_abs(g[b].cpu().numpy()[pos], ref[b, pos])
+            assert err <= tol, (b, name, err)
+
+
+def test_noalloc_bwd_falls_back_to_one_buffer_set(J):
+    """A problem whose two sets of segment buffers exceed the no-alloc scratch but one set fits:
+    the entry point that allocates nothing runs each prologue on its own and gives the bits of
+    the entry point with the larger workspace."""
+    import ctypes
+    import torch
+    B, S, Hq, Hkv, D, block, maxk, nseg = 1, 16384, 32, 8, 128, 128, 64, 4
+    nkb = S // block
+    kept = [np.sort(np.random.default_rng(77).choice(nkb, maxk, replace=False))]
+    g = torch.Generator(device="cuda").manual_seed(78)
+    qd = (torch.randn((B, S, Hq, D), generator=g, device="cuda") / 4).to(torch.bfloat16)
+    kd = (torch.randn((B, S, Hkv, D), generator=g, device="cuda") / 4).to(torch.bfloat16)
+    vd = torch.randn((B, S, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    dd = torch.randn((B, S, Hq, D), generator=g, device="cuda")
+    kept_d, nk_d = kept_tensor(kept, nkb)
+    p = J.make_problem(qd, kd, vd, block)
+    one = J.workspace_bytes(p, J.JENGA_OP_BWD_MIN, maxk, nseg)
+    assert one <= J.NOALLOC_SCRATCH_BYTES < J.workspace_bytes(p, J.JENGA_OP_BWD, maxk, nseg)
+    say(f"no-alloc backward with one buffer set: S{S} Hq{Hq} Hkv{Hkv} kept {maxk} N={nseg}")
+    resid = torch.zeros((B, S, Hq, D), device="cuda")
+    o_saved, lse = J.sparse_attn_fwd(qd, kd, vd, kept_d, nk_d, maxk, block, resid)
+    ref = J.sparse_attn_bwd(qd, kd, vd, kept_d, nk_d, maxk, block, o_saved, lse, dd, n_segments=nseg)
+    got = [torch.zeros_like(x) for x in ref]
+    st = J.lib.jenga_sparse_attn_bwd_segmented_noalloc(
+        ctypes.byref(p), qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), kept_d.data_ptr(),
+        nk_d.data_ptr(), maxk, o_saved.data_ptr(), lse.data_ptr(), dd.data_ptr(), got[0].data_ptr(),
+        got[1].data_ptr(), got[2].data_ptr(), nseg, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == J.JENGA_OK, J.status_string(st)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(a, b), name
+
+
 def test_empty_kept_set_is_noop(J):
     import torch
     B, S, Hq, Hkv, D, block, dtype = 1, 512, 2, 2, 128, 64, "bf16"

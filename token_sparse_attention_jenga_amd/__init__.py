@@ -32,6 +32,7 @@ JENGA_OP_SCORE = 0
 JENGA_OP_FWD = 1
 JENGA_OP_BWD = 2
 JENGA_OP_SCORE_EQ2 = 3
+JENGA_OP_BWD_MIN = 4
 
 EXPORTED = ["jenga_status_string", "jenga_topk_count", "jenga_workspace_bytes",
             "jenga_score_blocks", "jenga_score_blocks_eq2", "jenga_select_blocks",
@@ -395,8 +396,10 @@ def sparse_attn_fwd(q, k, v, kept_idx, n_kept, max_kept_blocks: int, block: int,
 
 
 def sparse_attn_bwd(q, k, v, kept_idx, n_kept, max_kept_blocks: int, block: int, o_saved, lse,
-                    dout, n_segments: int = 1, scale: float = 0.0, grads=None):
-    """Returns (dq, dk, dv) fp32; accumulates into `grads` when given."""
+                    dout, n_segments: int = 1, scale: float = 0.0, grads=None,
+                    min_workspace: bool = False):
+    """Returns (dq, dk, dv) fp32; accumulates into `grads` when given.  min_workspace: one set of
+    segment buffers (JENGA_OP_BWD_MIN) instead of the two of the faster schedule."""
     import torch
     p = make_problem(q, k, v, block, scale)
     if grads is None:
@@ -405,7 +408,8 @@ def sparse_attn_bwd(q, k, v, kept_idx, n_kept, max_kept_blocks: int, block: int,
         dv = torch.zeros(v.shape, dtype=torch.float32, device=q.device)
     else:
         dq, dk, dv = grads
-    ws = alloc_workspace(workspace_bytes(p, JENGA_OP_BWD, max_kept_blocks, n_segments), q.device)
+    op = JENGA_OP_BWD_MIN if min_workspace else JENGA_OP_BWD
+    ws = alloc_workspace(workspace_bytes(p, op, max_kept_blocks, n_segments), q.device)
     jenga_sparse_attn_bwd_segmented(p, q, k, v, kept_idx, n_kept, max_kept_blocks, o_saved, lse,
                                     dout, dq, dk, dv, n_segments, ws)
     return dq, dk, dv

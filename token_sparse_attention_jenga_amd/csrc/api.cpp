@@ -119,8 +119,24 @@ BwdLayout bwd_layout(const jenga_problem* p, int max_kept_blocks, int n_segments
   return o;
 }
 
-size_t bwd_ws_bytes(const jenga_problem* p, int max_kept_blocks, int n_segments) {
+// Segments the backward runs: the capacity max_kept_blocks * block cut into seg_len pieces.
+int bwd_segments_run(const jenga_problem* p, int max_kept_blocks, int n_segments) {
+  const int ncap = max_kept_blocks * p->block;
+  const int L = seg_len_of(ncap, n_segments);
+  return (ncap + L - 1) / L;
+}
+
+// The bf16 path with two or more segments takes two sets of one segment's buffers: the
+// prologue of segment s + 1 then runs inside the launch of segment s, writing the other set.
+// One set (bwd_ws_min_bytes) also works, with each prologue launched on its own.
+size_t bwd_ws_min_bytes(const jenga_problem* p, int max_kept_blocks, int n_segments) {
   return bwd_layout(p, max_kept_blocks, n_segments).total;
+}
+
+size_t bwd_ws_bytes(const jenga_problem* p, int max_kept_blocks, int n_segments) {
+  const size_t one = bwd_ws_min_bytes(p, max_kept_blocks, n_segments);
+  const bool two = p->dtype == JENGA_DTYPE_BF16 && bwd_segments_run(p, max_kept_blocks, n_segments) >= 2;
+  return two ? 2 * one : one;
 }
 
 size_t fwd_ws_bytes(const jenga_problem* p, int max_kept_blocks) {
@@ -295,11 +311,12 @@ size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks
     if (max_kept_blocks < 1 || max_kept_blocks > nkb) return 0;
     return fwd_ws_bytes(p, max_kept_blocks);
   }
-  if (op == JENGA_OP_BWD) {
+  if (op == JENGA_OP_BWD || op == JENGA_OP_BWD_MIN) {
     const int nkb = p->seq_len / p->block;
     if (max_kept_blocks < 1 || max_kept_blocks > nkb || n_segments < 1) return 0;
     if (n_segments > max_kept_blocks * p->block / 64) return 0;
-    return bwd_ws_bytes(p, max_kept_blocks, n_segments);
+    return op == JENGA_OP_BWD ? bwd_ws_bytes(p, max_kept_blocks, n_segments)
+                              : bwd_ws_min_bytes(p, max_kept_blocks, n_segments);
   }
   return 0;
 }
@@ -461,7 +478,8 @@ int bwd_segmented(const jenga_problem* p, const void* q, const void* k, const vo
   if (max_kept_blocks < 1 || max_kept_blocks > nkb) return JENGA_ERR_INVALID_ARG;
   const int ncap = max_kept_blocks * p->block;
   if (n_segments < 1 || n_segments > ncap / 64) return JENGA_ERR_INVALID_ARG;
-  const size_t need = bwd_ws_bytes(p, max_kept_blocks, n_segments);
+  const size_t need = bwd_ws_min_bytes(p, max_kept_blocks, n_segments);
+  const size_t need2 = bwd_ws_bytes(p, max_kept_blocks, n_segments);
   if (noalloc) {
     if (need > kNoAllocScratchBytes) return JENGA_ERR_SCRATCH_LIMIT;
     const int st2 = scratch_of_current_device(&workspace);
@@ -470,6 +488,8 @@ int bwd_segmented(const jenga_problem* p, const void* q, const void* k, const vo
   }
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
     return JENGA_ERR_WORKSPACE;
+  // two sets of segment buffers: each segment's launch also runs the next segment's prologue
+  const bool overlap = need2 > need && workspace_bytes >= need2;
   const int L = seg_len_of(ncap, n_segments);
   const BwdLayout lay = bwd_layout(p, max_kept_blocks, n_segments);
   jenga::BwdParams bp;
@@ -504,11 +524,40 @@ int bwd_segmented(const jenga_problem* p, const void* q, const void* k, const vo
   bp.scale = scale_of(p);
   bp.scale_log2 = bp.scale * 1.4426950408889634f;
   const bool fast = p->dtype == JENGA_DTYPE_BF16;
-  for (int s = 0; s < n_segments; ++s) {
-    if ((int64_t)s * L >= ncap) break;
+  const int nrun = bwd_segments_run(p, max_kept_blocks, n_segments);
+  const hipStream_t hs = (hipStream_t)stream;
+  if (overlap) {
+    // segment s reads buffer set s % 2; its launch fills set (s + 1) % 2 for segment s + 1
+    auto seg_params = [&](int s) {
+      jenga::BwdParams x = bp;
+      const size_t off = (s % 2) ? need : 0;
+      x.wsD = (float*)((char*)bp.wsD + off);
+      x.wsL2 = (float*)((char*)bp.wsL2 + off);
+      x.wsdO = (char*)bp.wsdO + off;
+      x.qtp = (char*)bp.qtp + off;
+      x.dotp = (char*)bp.dotp + off;
+      x.seg = s;
+      return x;
+    };
+    jenga::BwdParams cur = seg_params(0);
+    if (jenga::launch_prep64(cur, p->head_dim, hs) != hipSuccess) return JENGA_ERR_LAUNCH;
+    for (int s = 0; s < nrun; ++s) {
+      const jenga::BwdParams nxt = seg_params(s + 1);
+      if (jenga::launch_bwd64_main(cur, s + 1 < nrun ? &nxt : nullptr, p->head_dim, hs) != hipSuccess)
+        return JENGA_ERR_LAUNCH;
+      cur = nxt;
+    }
+    return JENGA_OK;
+  }
+  for (int s = 0; s < nrun; ++s) {
     bp.seg = s;
-    const hipError_t e = fast ? jenga::launch_bwd64_segment(bp, p->head_dim, (hipStream_t)stream)
-                              : jenga::launch_bwd_segment_f32(bp, (hipStream_t)stream);
+    hipError_t e;
+    if (fast) {
+      e = jenga::launch_prep64(bp, p->head_dim, hs);
+      if (e == hipSuccess) e = jenga::launch_bwd64_main(bp, nullptr, p->head_dim, hs);
+    } else {
+      e = jenga::launch_bwd_segment_f32(bp, hs);
+    }
     if (e != hipSuccess) return JENGA_ERR_LAUNCH;
   }
   return JENGA_OK;

@@ -37,11 +37,11 @@ struct PackArgs {
 
 // ------------------------------------------------------------------------------------------
 // Write a 32-row natural tile staged in LDS (row pitch D + 8 elements) as its TP tile [D][32]
-// at dst; the 256 threads of the workgroup write 16 bytes each per pass.
+// at dst; 256 threads (index tid) write 16 bytes each per pass.
 template <int D>
-__device__ __forceinline__ void write_tp_tile(const bf16* tile, char* dst) {
+__device__ __forceinline__ void write_tp_tile(const bf16* tile, char* dst, int tid) {
   constexpr int PITCH = D + 8;
-  for (int idx = threadIdx.x; idx < D * 4; idx += 256) {
+  for (int idx = tid; idx < D * 4; idx += 256) {
     const int d = idx >> 2, c = idx & 3;
     uint16_t v[8];
 #pragma unroll
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void k_pack_tp(PackArgs a) {
     *(u32x4*)(tile + row * PITCH + c * 8) = ld16(src + (int64_t)(pos0 + row) * a.s1 + c * 8);
   }
   __syncthreads();
-  write_tp_tile<D>(tile, (char*)a.dst + ((((int64_t)b * a.H + h) * a.tiles_per_head + t) * D) * 64);
+  write_tp_tile<D>(tile, (char*)a.dst + ((((int64_t)b * a.H + h) * a.tiles_per_head + t) * D) * 64, tid);
 }
 
 template <int D>
@@ -286,74 +286,97 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
 
 // ------------------------------------------------------------------------------------------
 // Backward prologue (one segment): D_i, dOut -> bf16 natural rows and TP tiles, and the TP
-// tiles of the same ranks' Q rows (one launch: each workgroup holds 32 ranks of one head)
+// tiles of the same ranks' Q rows.  One group = 32 ranks of one head, run by 256 threads.
 // ------------------------------------------------------------------------------------------
+constexpr int kPrepThreads = 256;
+constexpr int kPrepIters = 2;   // a workgroup of the fused backward launch runs 2 x this many groups
+
 template <int D>
-__global__ __launch_bounds__(256) void k_prep64(BwdParams p) {
+struct PrepLds {
+  static constexpr int PITCH = D + 8;                      // elements; breaks bank aliasing
+  static constexpr int TILE = 32 * PITCH * 2;              // bytes of one staged 32-row tile
+};
+
+// Group t of head h, batch row b (ranks seg * seg_len + 32 t ..), by the threads tid = 0..255
+// of a workgroup; tile and qtile are LDS arrays of PrepLds<D>::TILE bytes.  A thread with
+// `valid` false (or whose group lies past the segment's kept ranks) only takes part in the
+// barrier, which every thread of the workgroup reaches.
+template <int D>
+__device__ __forceinline__ void prep_group(const BwdParams& p, int t, int h, int b, int tid,
+                                           bf16* tile, bf16* qtile, bool valid) {
   constexpr int E = D / 8;                    // elements per thread (8 threads per row)
-  constexpr int PITCH = D + 8;
+  constexpr int PITCH = PrepLds<D>::PITCH;
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  constexpr int QC = 32 * CPR / 256;          // Q chunks per thread
-  __shared__ bf16 tile[32 * PITCH];
-  __shared__ bf16 qtile[32 * PITCH];
-  const int b = blockIdx.z, h = blockIdx.y, t = blockIdx.x, tid = threadIdx.x;
-  const int32_t* kept = p.kept + (int64_t)b * p.nkb;
-  const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
+  constexpr int QC = 32 * CPR / kPrepThreads; // Q chunks per thread
   const int qs = p.seg * p.seg_len;
-  const int qe = min(qs + p.seg_len, Nk);
   const int r0 = qs + 32 * t;
-  if (r0 >= qe) return;                       // qe - qs is a multiple of 64
-  const int pos0 = rank_to_pos(kept, p.block, r0);
-  // the Q rows' loads go out first; they land while dO . O is formed
-  const bf16* qsrc = (const bf16*)p.q + b * p.qs[0] + h * p.qs[2];
-  u32x4 qv[QC];
-#pragma unroll
-  for (int i = 0; i < QC; ++i) {
-    const int idx = tid + 256 * i, qr = idx / CPR, c = idx % CPR;
-    qv[i] = ld16(qsrc + (int64_t)(pos0 + qr) * p.qs[1] + c * 8);
+  if (valid) {                                // (b may be past the last batch row when not)
+    const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
+    valid = r0 < min(qs + p.seg_len, Nk);     // the kept ranks end on a multiple of 64
   }
-  const int row = tid >> 3, part = tid & 7;
-  const float* drow = p.dout + (((int64_t)b * p.S + pos0 + row) * p.Hq + h) * D + part * E;
-  const char* orow = (const char*)p.o_saved + ((((int64_t)b * p.ncap + r0 + row) * p.Hq + h) * D + part * E) * 2;
-  float dot = 0.f;
-  uint32_t packed[E / 2];
+  if (valid) {
+    const int32_t* kept = p.kept + (int64_t)b * p.nkb;
+    const int pos0 = rank_to_pos(kept, p.block, r0);
+    // the Q rows' loads go out first; they land while dO . O is formed
+    const bf16* qsrc = (const bf16*)p.q + b * p.qs[0] + h * p.qs[2];
+    u32x4 qv[QC];
 #pragma unroll
-  for (int c = 0; c < E / 8; ++c) {
-    const u32x4 ow = *(const u32x4*)(orow + c * 16);
-    const f32x4 d0 = *(const f32x4*)(drow + c * 8);
-    const f32x4 d1 = *(const f32x4*)(drow + c * 8 + 4);
-    dot += d0[0] * bf16_lo(ow[0]) + d0[1] * bf16_hi(ow[0]) + d0[2] * bf16_lo(ow[1]) +
-           d0[3] * bf16_hi(ow[1]) + d1[0] * bf16_lo(ow[2]) + d1[1] * bf16_hi(ow[2]) +
-           d1[2] * bf16_lo(ow[3]) + d1[3] * bf16_hi(ow[3]);
-    packed[4 * c + 0] = pack_bf16x2(d0[0], d0[1]);
-    packed[4 * c + 1] = pack_bf16x2(d0[2], d0[3]);
-    packed[4 * c + 2] = pack_bf16x2(d1[0], d1[1]);
-    packed[4 * c + 3] = pack_bf16x2(d1[2], d1[3]);
-  }
-  dot += __shfl_xor(dot, 4, 64);
-  dot += __shfl_xor(dot, 2, 64);
-  dot += __shfl_xor(dot, 1, 64);
-  const int rl = r0 - qs + row;
-  if (part == 0) {
-    p.wsD[((int64_t)b * p.Hq + h) * p.seg_len + rl] = dot;
-    p.wsL2[((int64_t)b * p.Hq + h) * p.seg_len + rl] = p.lse[((int64_t)b * p.Hq + h) * p.ncap + r0 + row] * kLog2e;
-  }
-  char* wrow = (char*)p.wsdO + ((((int64_t)b * p.seg_len + rl) * p.Hq + h) * D + part * E) * 2;
+    for (int i = 0; i < QC; ++i) {
+      const int idx = tid + kPrepThreads * i, qr = idx / CPR, c = idx % CPR;
+      qv[i] = ld16(qsrc + (int64_t)(pos0 + qr) * p.qs[1] + c * 8);
+    }
+    const int row = tid >> 3, part = tid & 7;
+    const float* drow = p.dout + (((int64_t)b * p.S + pos0 + row) * p.Hq + h) * D + part * E;
+    const char* orow = (const char*)p.o_saved + ((((int64_t)b * p.ncap + r0 + row) * p.Hq + h) * D + part * E) * 2;
+    float dot = 0.f;
+    uint32_t packed[E / 2];
 #pragma unroll
-  for (int c = 0; c < E / 8; ++c) {
-    u32x4 v = {packed[4 * c], packed[4 * c + 1], packed[4 * c + 2], packed[4 * c + 3]};
-    *(u32x4*)(wrow + c * 16) = v;
-    *(u32x4*)(tile + row * PITCH + part * E + c * 8) = v;
-  }
+    for (int c = 0; c < E / 8; ++c) {
+      const u32x4 ow = *(const u32x4*)(orow + c * 16);
+      const f32x4 d0 = *(const f32x4*)(drow + c * 8);
+      const f32x4 d1 = *(const f32x4*)(drow + c * 8 + 4);
+      dot += d0[0] * bf16_lo(ow[0]) + d0[1] * bf16_hi(ow[0]) + d0[2] * bf16_lo(ow[1]) +
+             d0[3] * bf16_hi(ow[1]) + d1[0] * bf16_lo(ow[2]) + d1[1] * bf16_hi(ow[2]) +
+             d1[2] * bf16_lo(ow[3]) + d1[3] * bf16_hi(ow[3]);
+      packed[4 * c + 0] = pack_bf16x2(d0[0], d0[1]);
+      packed[4 * c + 1] = pack_bf16x2(d0[2], d0[3]);
+      packed[4 * c + 2] = pack_bf16x2(d1[0], d1[1]);
+      packed[4 * c + 3] = pack_bf16x2(d1[2], d1[3]);
+    }
+    dot += __shfl_xor(dot, 4, 64);
+    dot += __shfl_xor(dot, 2, 64);
+    dot += __shfl_xor(dot, 1, 64);
+    const int rl = r0 - qs + row;
+    if (part == 0) {
+      p.wsD[((int64_t)b * p.Hq + h) * p.seg_len + rl] = dot;
+      p.wsL2[((int64_t)b * p.Hq + h) * p.seg_len + rl] = p.lse[((int64_t)b * p.Hq + h) * p.ncap + r0 + row] * kLog2e;
+    }
+    char* wrow = (char*)p.wsdO + ((((int64_t)b * p.seg_len + rl) * p.Hq + h) * D + part * E) * 2;
 #pragma unroll
-  for (int i = 0; i < QC; ++i) {
-    const int idx = tid + 256 * i, qr = idx / CPR, c = idx % CPR;
-    *(u32x4*)(qtile + qr * PITCH + c * 8) = qv[i];
+    for (int c = 0; c < E / 8; ++c) {
+      u32x4 v = {packed[4 * c], packed[4 * c + 1], packed[4 * c + 2], packed[4 * c + 3]};
+      *(u32x4*)(wrow + c * 16) = v;
+      *(u32x4*)(tile + row * PITCH + part * E + c * 8) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < QC; ++i) {
+      const int idx = tid + kPrepThreads * i, qr = idx / CPR, c = idx % CPR;
+      *(u32x4*)(qtile + qr * PITCH + c * 8) = qv[i];
+    }
   }
   __syncthreads();
-  const int64_t tp_tile = ((int64_t)b * p.Hq + h) * (p.seg_len / 32) + (r0 - qs) / 32;
-  write_tp_tile<D>(tile, (char*)p.dotp + tp_tile * D * 64);
-  write_tp_tile<D>(qtile, (char*)p.qtp + tp_tile * D * 64);
+  if (valid) {
+    const int64_t tp_tile = ((int64_t)b * p.Hq + h) * (p.seg_len / 32) + (r0 - qs) / 32;
+    write_tp_tile<D>(tile, (char*)p.dotp + tp_tile * D * 64, tid);
+    write_tp_tile<D>(qtile, (char*)p.qtp + tp_tile * D * 64, tid);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPrepThreads) void k_prep64(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char tile[PrepLds<D>::TILE];
+  __shared__ __attribute__((aligned(16))) char qtile[PrepLds<D>::TILE];
+  prep_group<D>(p, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, (bf16*)tile, (bf16*)qtile, true);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -776,9 +799,15 @@ static_assert(DKDV_NW == DQ_NW, "the fused backward launch runs both tile kinds 
 // The LDS buffers are separate arrays, shared by the two kinds (dQ: A, B, C; dK/dV: A, B and
 // the K rows): as distinct objects the compiler can tell that a direct-to-LDS load into one
 // buffer does not write another, and waits only for the loads of the buffer it reads.
+//
+// A third run may follow: the prologue of the next segment (pn, writing the other half of a
+// double workspace), two 32-rank groups per workgroup.  Dispatched last, these workgroups take
+// the compute units that the unequal tiles leave idle at the end of the launch, instead of a
+// launch of their own between the segments.
 // ------------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(64 * DQ_NW, 2) void k_bwd64(BwdParams pq, BwdParams pk, BwdGrid gr) {
+__global__ __launch_bounds__(64 * DQ_NW, 2) void k_bwd64(BwdParams pq, BwdParams pk, BwdGrid gr,
+                                                         BwdParams pn) {
   using KL = DkdvLds<D, DKDV_NW>;
   using QL = DqLds<D>;
   constexpr int AB = KL::STAGE > QL::STAGE ? KL::STAGE : QL::STAGE;
@@ -796,6 +825,20 @@ __global__ __launch_bounds__(64 * DQ_NW, 2) void k_bwd64(BwdParams pq, BwdParams
     const int i = lin - o, q = ((n + 7) >> 3);
     return (i & 7) * q + (i >> 3);
   };
+  if (lin >= gr.o_prep) {
+    static_assert(64 * DQ_NW == 2 * kPrepThreads && PrepLds<D>::TILE * 2 <= AB,
+                  "two prologue groups at a time, staged in buffers A and B");
+    const int half = threadIdx.x / kPrepThreads;
+    char* st = half ? bufB : bufA;
+    for (int it = 0; it < kPrepIters; ++it) {
+      if (it > 0) __syncthreads();                         // the staged tiles have been read
+      const int grp = 2 * (kPrepIters * (lin - gr.o_prep) + it) + half;   // (b Hq + h) ng + t
+      const int t = grp % gr.ng, h = (grp / gr.ng) % pn.Hq, b = grp / (gr.ng * pn.Hq);
+      prep_group<D>(pn, t, h, b, threadIdx.x - half * kPrepThreads, (bf16*)st,
+                    (bf16*)(st + PrepLds<D>::TILE), b < pn.B);
+    }
+    return;
+  }
   if (lin < gr.o_kv) {
     const int L = tile_of(0, gr.n_dq);
     if (L >= gr.n_dq) return;
@@ -832,18 +875,23 @@ hipError_t launch_fwd64(const FwdParams& p, int D, hipStream_t st) {
   return D == 64 ? launch_fwd64_t<64>(p, st) : launch_fwd64_t<128>(p, st);
 }
 
+// ranks of segment p.seg (capacity: max_kept_blocks * block, cut into seg_len pieces)
+static int seg_cap_of(const BwdParams& p) { return min(p.seg_len, p.ncap - p.seg * p.seg_len); }
+
 template <int D>
-static hipError_t bwd64_segment_t(const BwdParams& p, hipStream_t st) {
-  const int L = p.seg_len;
-  const int seg_cap = min(L, p.ncap - p.seg * L);          // ranks of this segment (capacity)
+static hipError_t prep64_t(const BwdParams& p, hipStream_t st) {
+  const int seg_cap = seg_cap_of(p);
   if (seg_cap <= 0) return hipSuccess;
-  hipError_t e;
-  {
-    TimedLaunch tl("k_prep64", st);
-    k_prep64<D><<<dim3((seg_cap + 31) / 32, p.Hq, p.B), 256, 0, st>>>(p);
-    e = hipGetLastError();
-  }
-  if (e != hipSuccess) return e;
+  TimedLaunch tl("k_prep64", st);
+  k_prep64<D><<<dim3((seg_cap + 31) / 32, p.Hq, p.B), kPrepThreads, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t bwd64_main_t(const BwdParams& p, const BwdParams* next, hipStream_t st) {
+  const int L = p.seg_len;
+  const int seg_cap = seg_cap_of(p);
+  if (seg_cap <= 0) return hipSuccess;
   const int seg_end = p.seg * L + seg_cap;
   constexpr int KG = 32 * DKDV_NW, QG = 32 * DQ_NB * DQ_NW;
   auto pad8 = [](int n) { return (n + 7) & ~7; };
@@ -853,14 +901,26 @@ static hipError_t bwd64_segment_t(const BwdParams& p, hipStream_t st) {
   gr.n_dq = gr.nqt * p.Hq * p.B;
   gr.n_kv = gr.nkt * p.Hkv * p.B;
   gr.o_kv = pad8(gr.n_dq);
-  const int nwg = gr.o_kv + pad8(gr.n_kv);
+  gr.o_prep = gr.o_kv + pad8(gr.n_kv);
+  gr.ng = 0;
+  int n_prep = 0;
+  const int next_cap = next ? seg_cap_of(*next) : 0;
+  if (next_cap > 0) {
+    gr.ng = (next_cap + 31) / 32;
+    constexpr int per_wg = 2 * kPrepIters;                 // groups per workgroup
+    n_prep = (gr.ng * next->Hq * next->B + per_wg - 1) / per_wg;
+  }
   TimedLaunch tl("k_bwd64", st);
-  k_bwd64<D><<<dim3(nwg), 64 * DQ_NW, 0, st>>>(p, p, gr);
+  k_bwd64<D><<<dim3(gr.o_prep + n_prep), 64 * DQ_NW, 0, st>>>(p, p, gr, next_cap > 0 ? *next : p);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd64_segment(const BwdParams& p, int D, hipStream_t st) {
-  return D == 64 ? bwd64_segment_t<64>(p, st) : bwd64_segment_t<128>(p, st);
+hipError_t launch_prep64(const BwdParams& p, int D, hipStream_t st) {
+  return D == 64 ? prep64_t<64>(p, st) : prep64_t<128>(p, st);
+}
+
+hipError_t launch_bwd64_main(const BwdParams& p, const BwdParams* next, int D, hipStream_t st) {
+  return D == 64 ? bwd64_main_t<64>(p, next, st) : bwd64_main_t<128>(p, next, st);
 }
 
 }  // namespace jenga

@@ -111,11 +111,14 @@ struct BwdParams {
 };
 
 // Workgroup runs of the fused backward launch of one segment (computed on the host): the dQ
-// tiles, then the dK/dV key tiles; o_kv is the launch offset of the second run (a multiple of 8).
+// tiles, then the dK/dV key tiles, then (when the next segment's prologue rides along) its
+// 32-rank groups, two per workgroup; o_kv and o_prep are the launch offsets of the second and
+// third runs (multiples of 8).
 struct BwdGrid {
   int nqt, nkt;                // dQ tiles per query head; dK/dV key tiles per KV head
-  int n_dq, n_kv;              // workgroups of each run (all heads and batch rows)
-  int o_kv;
+  int n_dq, n_kv;              // workgroups of the first two runs (all heads and batch rows)
+  int o_kv, o_prep;
+  int ng;                      // prologue groups per (batch row, head) of the next segment
 };
 
 
@@ -160,6 +163,10 @@ hipError_t timing_query(const char* name, int* launches, double* total_ms);
 
 // bf16 attention kernels (attn64.hip)
 hipError_t launch_fwd64(const FwdParams& p, int D, hipStream_t st);
-hipError_t launch_bwd64_segment(const BwdParams& p, int D, hipStream_t st);
+// One segment's backward: the prologue of segment p.seg (launch_prep64), then its dQ and dK/dV
+// tiles (launch_bwd64_main).  With `next` given, the main launch also runs the prologue of
+// segment next->seg, which must write a workspace other than p's.
+hipError_t launch_prep64(const BwdParams& p, int D, hipStream_t st);
+hipError_t launch_bwd64_main(const BwdParams& p, const BwdParams* next, int D, hipStream_t st);
 
 }  // namespace jenga
