@@ -211,11 +211,16 @@ int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, 
  *   dk, dv            [B][S][Hkv][D] fp32, dense, accumulated (+=) at kept rows only
  *   n_segments        1 <= n_segments <= max_kept_blocks*block/64
  *   workspace         >= jenga_workspace_bytes(p, JENGA_OP_BWD_MIN, max_kept_blocks, n_segments)
- *                     bytes, 256-byte aligned.  bf16 with two or more segments: a workspace of
- *                     jenga_workspace_bytes(p, JENGA_OP_BWD, ...) = twice that holds two sets
- *                     of segment buffers, and each segment's launch then also runs the next
- *                     segment's prologue; with less, every prologue is a launch of its own.
- *                     Both schedules give the same bits.
+ *                     bytes, 256-byte aligned: one set of segment buffers, plus (bf16) slots
+ *                     for the parts of long dK/dV key tiles (below).  bf16 with two or more
+ *                     segments: jenga_workspace_bytes(p, JENGA_OP_BWD, ...) adds a second set,
+ *                     and each segment's launch then also runs the next segment's prologue;
+ *                     with less, every prologue is a launch of its own.  Both schedules give
+ *                     the same bits.
+ * bf16: a dK/dV key tile (256 kept keys of one KV head) loops over the segment's queries of
+ * every query head of its group.  When that loop is longer than the launch's average load per
+ * compute unit (grouped-query attention in few segments), the tile runs in parts; the first
+ * adds into dk/dv, the others' sums are added after the launch in part order.
  * bf16: every gradient is accumulated by a fixed schedule, so results repeat bit for bit.
  * fp32: dq receives fp32 atomic additions, so its low bits may differ run to run.
  */

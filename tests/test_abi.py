@@ -167,6 +167,13 @@ def test_workspace_scales_with_segments_and_kept_blocks(J):
     # bf16 with two or more segments: the faster schedule takes two sets of segment buffers
     assert J.workspace_bytes(p, J.JENGA_OP_BWD, 128, 8) == 2 * w8
     assert J.workspace_bytes(p, J.JENGA_OP_BWD, 64, 8) == 2 * w8_half
+    # grouped-query attention in one segment (32/8 heads, 90 kept blocks of 64): the long dK/dV
+    # key tiles run in parts, whose sums need slots beyond the segment buffers
+    pg = _problem(J, S=16384, Hq=32, Hkv=8, D=128, block=64, dtype=1)
+    one_g = J.workspace_bytes(pg, J.JENGA_OP_BWD_MIN, 90, 1)
+    assert one_g > seg(5760)
+    assert (one_g - seg(5760)) % (2 * 256 * 128 * 4 * 8) == 0          # whole slots per KV head
+    assert J.workspace_bytes(pg, J.JENGA_OP_BWD, 90, 1) == one_g         # one segment: one set
     p32 = _problem(J, S=4096, Hq=4, Hkv=4, D=64, block=64, dtype=0)
     assert J.workspace_bytes(p32, J.JENGA_OP_BWD, 32, 4) == J.workspace_bytes(p32, J.JENGA_OP_BWD_MIN, 32, 4)
     assert J.workspace_bytes(p, J.JENGA_OP_FWD, 128) == vtp

@@ -190,7 +190,16 @@ SCHED_CASES = [
     (2, 4096, 4, 2, 128, 64, (40, 26), 40, 3),   # short last segment; row 1 ends in segment 1
     (1, 2048, 3, 1, 64, 128, (16,), 16, 4),       # grouped-query attention, head_dim 64
     (1, 1024, 1, 1, 128, 64, (8,), 8, 8),         # two prologue groups per segment: a workgroup
-]                                                 # of the fused launch with idle halves
+                                                  # of the fused launch with idle halves
+    # grouped-query attention where long dK/dV key tiles run in parts (sums of parts 1.. added
+    # after the launch): one segment, the first key tiles in five parts
+    (1, 8192, 8, 2, 128, 64, (40,), 40, 1),
+    # four query heads per KV head, head_dim 64: row 1 ends before the last key tiles, whose
+    # parts then do not run
+    (2, 4096, 4, 1, 64, 64, (30, 18), 30, 1),
+    # split key tiles with two sets of segment buffers
+    (1, 4096, 8, 2, 128, 64, (48,), 48, 2),
+]
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,D,block,counts,maxk,nseg", SCHED_CASES)
@@ -211,7 +220,7 @@ def test_bwd_schedules_bitwise(J, B, S, Hq, Hkv, D, block, counts, maxk, nseg):
     dd = torch.from_numpy(dout).cuda()
     p = J.make_problem(qd, kd, vd, block)
     one = J.workspace_bytes(p, J.JENGA_OP_BWD_MIN, maxk, nseg)
-    assert J.workspace_bytes(p, J.JENGA_OP_BWD, maxk, nseg) == 2 * one
+    assert (J.workspace_bytes(p, J.JENGA_OP_BWD, maxk, nseg) > one) == (nseg > 1)   # a second set
     got = [J.sparse_attn_bwd(qd, kd, vd, kept_d, nk_d, maxk, block, o_saved, lse, dd, n_segments=nseg,
                              min_workspace=lean) for lean in (False, True)]
     torch.cuda.synchronize()
@@ -232,7 +241,7 @@ def test_noalloc_bwd_falls_back_to_one_buffer_set(J):
     the entry point with the larger workspace."""
     import ctypes
     import torch
-    B, S, Hq, Hkv, D, block, maxk, nseg = 1, 16384, 32, 8, 128, 128, 64, 4
+    B, S, Hq, Hkv, D, block, maxk, nseg = 1, 16384, 32, 32, 128, 128, 64, 4
     nkb = S // block
     kept = [np.sort(np.random.default_rng(77).choice(nkb, maxk, replace=False))]
     g = torch.Generator(device="cuda").manual_seed(78)

@@ -126,17 +126,34 @@ int bwd_segments_run(const jenga_problem* p, int max_kept_blocks, int n_segments
   return (ncap + L - 1) / L;
 }
 
+// Slots for the parts of split dK/dV tiles (bf16): the most any segment needs, since the
+// segments run one after another and each one's slots are added up before the next starts.
+size_t bwd_kv_slot_bytes(const jenga_problem* p, int max_kept_blocks, int n_segments) {
+  if (p->dtype != JENGA_DTYPE_BF16) return 0;
+  const int ncap = max_kept_blocks * p->block;
+  const int L = seg_len_of(ncap, n_segments);
+  const int G = p->n_heads_q / p->n_heads_kv;
+  int most = 0;
+  for (int s = 0; s < bwd_segments_run(p, max_kept_blocks, n_segments); ++s) {
+    const int qs = s * L, cap = std::min(L, ncap - qs);
+    const int target = jenga::kv_split_target(qs, cap, G, p->n_heads_q, p->n_heads_kv, p->batch);
+    most = std::max(most, jenga::kv_split_extra(qs, cap, G, target));
+  }
+  return align_up((size_t)p->batch * p->n_heads_kv * most * 2 * jenga::kKvKeys * p->head_dim * sizeof(float));
+}
+
 // The bf16 path with two or more segments takes two sets of one segment's buffers: the
 // prologue of segment s + 1 then runs inside the launch of segment s, writing the other set.
-// One set (bwd_ws_min_bytes) also works, with each prologue launched on its own.
+// One set (bwd_ws_min_bytes) also works, with each prologue launched on its own.  The slots of
+// split dK/dV tiles follow the sets.
 size_t bwd_ws_min_bytes(const jenga_problem* p, int max_kept_blocks, int n_segments) {
-  return bwd_layout(p, max_kept_blocks, n_segments).total;
+  return bwd_layout(p, max_kept_blocks, n_segments).total + bwd_kv_slot_bytes(p, max_kept_blocks, n_segments);
 }
 
 size_t bwd_ws_bytes(const jenga_problem* p, int max_kept_blocks, int n_segments) {
-  const size_t one = bwd_ws_min_bytes(p, max_kept_blocks, n_segments);
+  const size_t one = bwd_layout(p, max_kept_blocks, n_segments).total;
   const bool two = p->dtype == JENGA_DTYPE_BF16 && bwd_segments_run(p, max_kept_blocks, n_segments) >= 2;
-  return two ? 2 * one : one;
+  return (two ? 2 * one : one) + bwd_kv_slot_bytes(p, max_kept_blocks, n_segments);
 }
 
 size_t fwd_ws_bytes(const jenga_problem* p, int max_kept_blocks) {
@@ -492,6 +509,7 @@ int bwd_segmented(const jenga_problem* p, const void* q, const void* k, const vo
   const bool overlap = need2 > need && workspace_bytes >= need2;
   const int L = seg_len_of(ncap, n_segments);
   const BwdLayout lay = bwd_layout(p, max_kept_blocks, n_segments);
+  const size_t set_bytes = lay.total;              // one set of segment buffers
   jenga::BwdParams bp;
   bp.q = q;
   bp.k = k;
@@ -512,6 +530,7 @@ int bwd_segmented(const jenga_problem* p, const void* q, const void* k, const vo
   bp.wsdO = (char*)workspace + lay.dO;
   bp.qtp = (char*)workspace + lay.qtp;
   bp.dotp = (char*)workspace + lay.dotp;
+  bp.wsKv = (float*)((char*)workspace + (overlap ? 2 : 1) * set_bytes);
   bp.B = p->batch;
   bp.S = p->seq_len;
   bp.Hq = p->n_heads_q;
@@ -530,7 +549,7 @@ int bwd_segmented(const jenga_problem* p, const void* q, const void* k, const vo
     // segment s reads buffer set s % 2; its launch fills set (s + 1) % 2 for segment s + 1
     auto seg_params = [&](int s) {
       jenga::BwdParams x = bp;
-      const size_t off = (s % 2) ? need : 0;
+      const size_t off = (s % 2) ? set_bytes : 0;
       x.wsD = (float*)((char*)bp.wsD + off);
       x.wsL2 = (float*)((char*)bp.wsL2 + off);
       x.wsdO = (char*)bp.wsdO + off;

@@ -18,6 +18,8 @@
 //   k_bwd64     one launch per segment with two kinds of workgroup tiles (no atomics):
 //                 dK/dV, key-major:   S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q
 //                 dQ, query-major:    S^T = K Q^T, dP^T = V dO^T, dQ += dS K
+//               and, when two sets of segment buffers are given, the next segment's prologue
+//   k_kv_reduce after a launch whose long dK/dV tiles ran in parts: adds the parts' sums
 #include "common.h"
 #include "kernels.h"
 #include "tiles64.h"
@@ -393,10 +395,12 @@ struct DkdvLds {
   static constexpr int KROWS = NW * C::NAT32;                   // the workgroup's K rows
 };
 
-// key tile tx (32 * NW kept keys) of KV head g, batch row b
+// key tile tx (32 * NW kept keys) of KV head g, batch row b; part `part` of `nparts` runs the
+// steps [part * n / nparts, (part + 1) * n / nparts) of the tile's n steps and adds into dk/dv
+// (part 0, slot null) or writes its sums to `slot` ([2][32 NW][D]: dK scaled, then dV)
 template <int D, int NW>
 __device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB, char* sK, int* ktab,
-                                          int tx, int g, int b) {
+                                          int tx, int g, int b, int part, int nparts, float* slot) {
   using C = T64<D>;
   using LY = DkdvLds<D, NW>;
   constexpr int KEYS = 32 * NW;
@@ -540,17 +544,18 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB
     SCHED_READS_AHEAD(2 * C::NDB, 2, 2, 1);
   };
 
-  if (nsteps > 0) {
-    issue(0, sA);
+  const int s0 = part * nsteps / nparts, s1 = (part + 1) * nsteps / nparts;
+  if (s1 > s0) {
+    issue(s0, sA);
     wait_all_mem();
     __syncthreads();
-    for (int step = 0; step < nsteps; step += 2) {
-      if (step + 1 < nsteps) issue(step + 1, sB);
+    for (int step = s0; step < s1; step += 2) {
+      if (step + 1 < s1) issue(step + 1, sB);
       compute(step, sA);
       wait_all_mem();
       stage_barrier();
-      if (step + 1 >= nsteps) break;
-      if (step + 2 < nsteps) issue(step + 2, sA);
+      if (step + 1 >= s1) break;
+      if (step + 2 < s1) issue(step + 2, sA);
       compute(step + 1, sB);
       wait_all_mem();
       stage_barrier();
@@ -558,6 +563,21 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB
   }
 
   if (!key_valid) return;
+  if (slot) {
+    // row w * 32 + 8(r/4) + 4hl + r%4 of the tile, column db*32 + lc
+    float* const sk = slot + (w * 32 + 4 * hl) * D + lc;
+    float* const sv = sk + KEYS * D;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          sk[(8 * rg + i) * D + db * 32] = p.scale * dk[db][4 * rg + i];
+          sv[(8 * rg + i) * D + db * 32] = dv[db][4 * rg + i];
+        }
+    return;
+  }
   // dK (scaled), dV += accumulators; lane holds head_dim column db*32 + lc of keys
   // kw0 + 8(r/4) + 4hl + r%4.  Reads are issued in two batches of 8 rows.  The wave's 32 kept
   // ranks lie in one kept block (blocks are multiples of 64 rows), so one lookup places them
@@ -776,6 +796,7 @@ constexpr int DKDV_NW = 8;
 constexpr int DQ_NB = 1, DQ_NW = 8;
 constexpr int kKvWeightOrderMax = 128;   // dK/dV tiles per XCD up to which they go weight-major
 static_assert(DKDV_NW == DQ_NW, "the fused backward launch runs both tile kinds in one workgroup shape");
+static_assert(32 * DKDV_NW == kKvKeys, "the split plan counts 256-key dK/dV tiles");
 
 // ------------------------------------------------------------------------------------------
 // One segment's dQ tiles and dK/dV tiles in one launch.  Each kind alone fills the GPU with
@@ -805,7 +826,9 @@ static_assert(DKDV_NW == DQ_NW, "the fused backward launch runs both tile kinds 
 // the compute units that the unequal tiles leave idle at the end of the launch, instead of a
 // launch of their own between the segments.
 // ------------------------------------------------------------------------------------------
-template <int D>
+// SPLIT: some dK/dV tiles run in parts (then the dK/dV run goes first).  A launch without
+// split tiles runs the instance without that code, as compiled before parts existed.
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(64 * DQ_NW, 2) void k_bwd64(BwdParams pq, BwdParams pk, BwdGrid gr,
                                                          BwdParams pn) {
   using KL = DkdvLds<D, DKDV_NW>;
@@ -839,24 +862,101 @@ __global__ __launch_bounds__(64 * DQ_NW, 2) void k_bwd64(BwdParams pq, BwdParams
     }
     return;
   }
-  if (lin < gr.o_kv) {
-    const int L = tile_of(0, gr.n_dq);
+  if (SPLIT ? lin >= ((gr.n_kv + 7) & ~7) : lin < gr.o_kv) {
+    const int L = SPLIT ? tile_of(gr.o_dq, gr.n_dq) : tile_of(0, gr.n_dq);
     if (L >= gr.n_dq) return;
     dq_tile<D, DQ_NB, DQ_NW>(pq, bufA, bufB, bufC, ktab, L % gr.nqt, (L / gr.nqt) % pq.Hq,
                              L / (gr.nqt * pq.Hq));
   } else {
     const int i = lin - gr.o_kv, q = (gr.n_kv + 7) >> 3, x = i & 7, j = i >> 3;
     int L;
-    if (q <= kKvWeightOrderMax && q % gr.nkt == 0) {
-      const int rows = q / gr.nkt;               // (batch, head) rows of XCD x's range
-      L = (x * rows + j % rows) * gr.nkt + j / rows;
+    if (q <= kKvWeightOrderMax && q % gr.nki == 0) {
+      const int rows = q / gr.nki;               // (batch, head) rows of XCD x's range
+      L = (x * rows + j % rows) * gr.nki + j / rows;
     } else {
       L = x * q + j;                             // = tile_of(gr.o_kv, gr.n_kv)
     }
     if (L >= gr.n_kv) return;
-    dkdv_tile<D, DKDV_NW>(pk, bufA, bufB, bufK, ktab, L % gr.nkt, (L / gr.nkt) % pk.Hkv,
-                          L / (gr.nkt * pk.Hkv));
+    // item of its (batch row, KV head): the parts of key tile 0, then of tile 1, ...
+    const int item = L % gr.nki, g = (L / gr.nki) % pk.Hkv, b = L / (gr.nki * pk.Hkv);
+    int tx = item, part = 0, nparts = 1;
+    float* slot = nullptr;
+    if constexpr (SPLIT) {
+      const int qs = pk.seg * pk.seg_len, G = pk.Hq / pk.Hkv;
+      int first = 0, extra = 0;
+      for (tx = 0;; ++tx) {
+        nparts = kv_tile_parts(kv_tile_steps(tx, qs, gr.seg_end, G), gr.kv_target);
+        if (item < first + nparts) break;
+        first += nparts;
+        extra += nparts - 1;
+      }
+      part = item - first;
+      if (part > 0)
+        slot = pk.wsKv + (((int64_t)b * pk.Hkv + g) * gr.n_extra + extra + part - 1) * (2 * kKvKeys * D);
+    }
+    dkdv_tile<D, DKDV_NW>(pk, bufA, bufB, bufK, ktab, tx, g, b, part, nparts, slot);
   }
+}
+
+// Adds the slots of the split dK/dV tiles of one segment into dk/dv, parts 1.. in order, after
+// the launch in which part 0 added its own sums.  One workgroup per key tile (tiles run in one
+// part exit at once).
+template <int D>
+__global__ __launch_bounds__(256) void k_kv_reduce(BwdParams p, BwdGrid gr) {
+  const int tx = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int qs = p.seg * p.seg_len, G = p.Hq / p.Hkv;
+  int extra = 0;
+  for (int t = 0; t < tx; ++t) extra += kv_tile_parts(kv_tile_steps(t, qs, gr.seg_end, G), gr.kv_target) - 1;
+  const int P = kv_tile_parts(kv_tile_steps(tx, qs, gr.seg_end, G), gr.kv_target);
+  if (P <= 1) return;
+  const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
+  const int qe = min(qs + p.seg_len, Nk);
+  const int k0 = tx * kKvKeys;
+  if (qs >= qe || k0 >= qe) return;                    // the tile's parts did not run
+  const int rows = min(kKvKeys, Nk - k0);              // its kept keys (a multiple of 64)
+  const float* const s0 = p.wsKv + (((int64_t)b * p.Hkv + g) * gr.n_extra + extra) * (2 * kKvKeys * D);
+  const int32_t* kept = p.kept + (int64_t)b * p.nkb;
+  for (int e = threadIdx.x; e < rows * D; e += 256) {
+    const int r = e / D, d = e - r * D, rank = k0 + r;
+    const int pos = kept[rank / p.block] * p.block + rank % p.block;
+    const int64_t o = (((int64_t)b * p.S + pos) * p.Hkv + g) * D + d;
+    float xk = p.dk[o], xv = p.dv[o];
+    for (int q = 0; q < P - 1; ++q) {
+      const float* sl = s0 + (int64_t)q * (2 * kKvKeys * D);
+      xk += sl[r * D + d];
+      xv += sl[kKvKeys * D + r * D + d];
+    }
+    p.dk[o] = xk;
+    p.dv[o] = xv;
+  }
+}
+
+int kv_split_target(int qs, int seg_cap, int G, int Hq, int Hkv, int B) {
+  const int seg_end = qs + seg_cap;
+  int64_t kv = 0, dq = 0;
+  int longest = 0;
+  for (int tx = 0; tx * kKvKeys < seg_end; ++tx) {
+    const int st = kv_tile_steps(tx, qs, seg_end, G);
+    kv += st;
+    longest = max(longest, st);
+  }
+  for (int q0 = qs; q0 < seg_end; q0 += 32 * DQ_NB * DQ_NW) dq += (min(q0 + 32 * DQ_NB * DQ_NW, seg_end) - 1) / 32 + 1;
+  // load per compute unit in dK/dV steps (a dQ step runs 24 MFMAs per wave, a dK/dV step 32)
+  const double per_cu = ((double)kv * Hkv * B + 0.75 * (double)dq * Hq * B) / kComputeUnits;
+  // only a tile longer than that load sets the launch's length; its parts, at most half the
+  // load, let the launch pack its work evenly (128 steps or more each, so that light launches
+  // do not spend much workspace on many small parts)
+  if (longest <= per_cu) return 0;
+  const int target = max(128, (int)(per_cu / 2));
+  return longest > target ? target : 0;
+}
+
+int kv_split_extra(int qs, int seg_cap, int G, int target) {
+  if (target <= 0) return 0;
+  const int seg_end = qs + seg_cap;
+  int extra = 0;
+  for (int tx = 0; tx * kKvKeys < seg_end; ++tx) extra += kv_tile_parts(kv_tile_steps(tx, qs, seg_end, G), target) - 1;
+  return extra;
 }
 
 template <int D>
@@ -899,9 +999,19 @@ static hipError_t bwd64_main_t(const BwdParams& p, const BwdParams* next, hipStr
   gr.nqt = (seg_cap + QG - 1) / QG;
   gr.nkt = (seg_end + KG - 1) / KG;
   gr.n_dq = gr.nqt * p.Hq * p.B;
-  gr.n_kv = gr.nkt * p.Hkv * p.B;
-  gr.o_kv = pad8(gr.n_dq);
-  gr.o_prep = gr.o_kv + pad8(gr.n_kv);
+  gr.seg_end = seg_end;
+  const int G = p.Hq / p.Hkv;
+  gr.kv_target = kv_split_target(p.seg * L, seg_cap, G, p.Hq, p.Hkv, p.B);
+  gr.n_extra = kv_split_extra(p.seg * L, seg_cap, G, gr.kv_target);
+  gr.nki = gr.nkt + gr.n_extra;
+  gr.n_kv = gr.nki * p.Hkv * p.B;
+  // dQ tiles first, heaviest first; but when dK/dV tiles run in parts, those parts are the
+  // longest work of the launch and go first (16K-token GQA layer, one segment: 1.44 -> 1.26 ms
+  // against dQ first, both split)
+  const bool split = gr.n_extra > 0;
+  gr.o_kv = split ? 0 : pad8(gr.n_dq);
+  gr.o_dq = split ? pad8(gr.n_kv) : 0;
+  gr.o_prep = pad8(gr.n_dq) + pad8(gr.n_kv);
   gr.ng = 0;
   int n_prep = 0;
   const int next_cap = next ? seg_cap_of(*next) : 0;
@@ -910,8 +1020,18 @@ static hipError_t bwd64_main_t(const BwdParams& p, const BwdParams* next, hipStr
     constexpr int per_wg = 2 * kPrepIters;                 // groups per workgroup
     n_prep = (gr.ng * next->Hq * next->B + per_wg - 1) / per_wg;
   }
-  TimedLaunch tl("k_bwd64", st);
-  k_bwd64<D><<<dim3(gr.o_prep + n_prep), 64 * DQ_NW, 0, st>>>(p, p, gr, next_cap > 0 ? *next : p);
+  {
+    TimedLaunch tl("k_bwd64", st);
+    const dim3 grid(gr.o_prep + n_prep);
+    if (split)
+      k_bwd64<D, true><<<grid, 64 * DQ_NW, 0, st>>>(p, p, gr, next_cap > 0 ? *next : p);
+    else
+      k_bwd64<D, false><<<grid, 64 * DQ_NW, 0, st>>>(p, p, gr, next_cap > 0 ? *next : p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || gr.n_extra == 0) return e;
+  }
+  TimedLaunch tl("k_kv_reduce", st);
+  k_kv_reduce<D><<<dim3(gr.nkt, p.Hkv, p.B), 256, 0, st>>>(p, gr);
   return hipGetLastError();
 }
 

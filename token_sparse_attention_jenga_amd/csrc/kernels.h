@@ -106,6 +106,7 @@ struct BwdParams {
   void* wsdO;    // [B][L][Hq][D] dOut rows of the segment in operand dtype, by kept rank
   void* qtp;     // bf16 path: [B][Hq][L/32] TP tiles of the segment's Q rows
   void* dotp;    // bf16 path: [B][Hq][L/32] TP tiles of the segment's dOut rows (bf16)
+  float* wsKv;   // bf16 path: [B][Hkv][extra parts][2][256][D] sums of split dK/dV tiles
   int B, S, Hq, Hkv, block, nkb, max_kept_blocks, ncap, seg_len, seg;
   float scale, scale_log2;
 };
@@ -117,9 +118,38 @@ struct BwdParams {
 struct BwdGrid {
   int nqt, nkt;                // dQ tiles per query head; dK/dV key tiles per KV head
   int n_dq, n_kv;              // workgroups of the first two runs (all heads and batch rows)
-  int o_kv, o_prep;
+  int o_dq, o_kv, o_prep;
   int ng;                      // prologue groups per (batch row, head) of the next segment
+  int seg_end;                 // end of the segment's ranks at full capacity
+  int kv_target;               // steps per part of a split dK/dV tile (0: no tile is split)
+  int nki, n_extra;            // dK/dV workgroups and extra parts per (batch row, KV head)
 };
+
+// Long dK/dV key tiles of the bf16 backward run in parts.  A key tile's steps are the query
+// rows of the segment at or after its keys (32 per step) times the query heads of its KV
+// group; at full capacity its step count follows from the segment alone.  When a tile would
+// have more steps than the launch's average load per compute unit (grouped-query attention
+// with one segment: the first key tiles take every query of four heads), it runs as parts over
+// consecutive ranges of its steps.  Part 0 adds into dk/dv as a whole tile does;
+// parts 1.. write their sums to slots, which k_kv_reduce adds after the launch in part order --
+// a fixed order, so results still repeat bit for bit.
+constexpr int kKvKeys = 256;           // keys per dK/dV tile (8 waves x 32)
+constexpr int kKvMaxParts = 8;
+constexpr int kComputeUnits = 256;     // MI355X
+
+__host__ __device__ inline int kv_tile_steps(int tx, int qs, int seg_end, int G) {
+  const int from = qs > kKvKeys * tx ? qs : kKvKeys * tx;
+  return from < seg_end ? G * ((seg_end - from) / 32) : 0;
+}
+__host__ __device__ inline int kv_tile_parts(int steps, int target) {
+  if (target <= 0) return 1;
+  const int n = (steps + target - 1) / target;
+  return n < 1 ? 1 : (n > kKvMaxParts ? kKvMaxParts : n);
+}
+// Steps per part for the segment of ranks [qs, qs + seg_cap) (0: no split), and the extra
+// parts per (batch row, KV head) it makes.
+int kv_split_target(int qs, int seg_cap, int G, int Hq, int Hkv, int B);
+int kv_split_extra(int qs, int seg_cap, int G, int target);
 
 
 // dtype: 0 = fp32 operands, 1 = bf16 operands.  Each returns hipGetLastError().
