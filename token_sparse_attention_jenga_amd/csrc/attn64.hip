@@ -899,11 +899,19 @@ __global__ __launch_bounds__(64 * DQ_NW, 2) void k_bwd64(BwdParams pq, BwdParams
 }
 
 // Adds the slots of the split dK/dV tiles of one segment into dk/dv, parts 1.. in order, after
-// the launch in which part 0 added its own sums.  One workgroup per key tile (tiles run in one
-// part exit at once).
+// the launch in which part 0 added its own sums.  One workgroup per 32 rows of a key tile (tiles
+// run in one part exit at once); each thread takes four runs of 4 floats, all loads issued
+// before the sums are formed (16-byte loads from the slots; dk and dv, which need only 4-byte
+// alignment, by the float).
+constexpr int kKvReduceRows = 32;
+
 template <int D>
 __global__ __launch_bounds__(256) void k_kv_reduce(BwdParams p, BwdGrid gr) {
-  const int tx = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  constexpr int PIECES = kKvReduceRows * D / 4;             // float4 pieces per workgroup
+  constexpr int PER = PIECES / 256;                         // per thread (4 at D = 128)
+  static_assert(PER * 256 == PIECES, "whole pieces per thread");
+  const int tx = blockIdx.x / (kKvKeys / kKvReduceRows), rg = blockIdx.x % (kKvKeys / kKvReduceRows);
+  const int g = blockIdx.y, b = blockIdx.z;
   const int qs = p.seg * p.seg_len, G = p.Hq / p.Hkv;
   int extra = 0;
   for (int t = 0; t < tx; ++t) extra += kv_tile_parts(kv_tile_steps(t, qs, gr.seg_end, G), gr.kv_target) - 1;
@@ -911,24 +919,48 @@ __global__ __launch_bounds__(256) void k_kv_reduce(BwdParams p, BwdGrid gr) {
   if (P <= 1) return;
   const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
   const int qe = min(qs + p.seg_len, Nk);
-  const int k0 = tx * kKvKeys;
-  if (qs >= qe || k0 >= qe) return;                    // the tile's parts did not run
-  const int rows = min(kKvKeys, Nk - k0);              // its kept keys (a multiple of 64)
+  const int k0 = tx * kKvKeys, r0 = rg * kKvReduceRows;
+  if (qs >= qe || k0 >= qe || k0 + r0 >= Nk) return;        // the tile's parts did not run
+  // (kept keys of a tile end on a multiple of 64, so these 32 rows are all kept)
   const float* const s0 = p.wsKv + (((int64_t)b * p.Hkv + g) * gr.n_extra + extra) * (2 * kKvKeys * D);
   const int32_t* kept = p.kept + (int64_t)b * p.nkb;
-  for (int e = threadIdx.x; e < rows * D; e += 256) {
-    const int r = e / D, d = e - r * D, rank = k0 + r;
+  f32x4 xk[PER], xv[PER];
+  int64_t off[PER];
+  int so[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = threadIdx.x + 256 * i, r = r0 + c / (D / 4), d = 4 * (c % (D / 4));
+    const int rank = k0 + r;
     const int pos = kept[rank / p.block] * p.block + rank % p.block;
-    const int64_t o = (((int64_t)b * p.S + pos) * p.Hkv + g) * D + d;
-    float xk = p.dk[o], xv = p.dv[o];
-    for (int q = 0; q < P - 1; ++q) {
-      const float* sl = s0 + (int64_t)q * (2 * kKvKeys * D);
-      xk += sl[r * D + d];
-      xv += sl[kKvKeys * D + r * D + d];
+    off[i] = (((int64_t)b * p.S + pos) * p.Hkv + g) * D + d;
+    so[i] = r * D + d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xk[i][e] = p.dk[off[i] + e];
+      xv[i][e] = p.dv[off[i] + e];
     }
-    p.dk[o] = xk;
-    p.dv[o] = xv;
   }
+  for (int q = 0; q < P - 1; ++q) {
+    const float* sl = s0 + (int64_t)q * (2 * kKvKeys * D);
+    f32x4 ak[PER], av[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      ak[i] = *(const f32x4*)(sl + so[i]);
+      av[i] = *(const f32x4*)(sl + kKvKeys * D + so[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      xk[i] += ak[i];
+      xv[i] += av[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p.dk[off[i] + e] = xk[i][e];
+      p.dv[off[i] + e] = xv[i][e];
+    }
 }
 
 int kv_split_target(int qs, int seg_cap, int G, int Hq, int Hkv, int B) {
@@ -1031,7 +1063,7 @@ static hipError_t bwd64_main_t(const BwdParams& p, const BwdParams* next, hipStr
     if (e != hipSuccess || gr.n_extra == 0) return e;
   }
   TimedLaunch tl("k_kv_reduce", st);
-  k_kv_reduce<D><<<dim3(gr.nkt, p.Hkv, p.B), 256, 0, st>>>(p, gr);
+  k_kv_reduce<D><<<dim3(gr.nkt * (kKvKeys / kKvReduceRows), p.Hkv, p.B), 256, 0, st>>>(p, gr);
   return hipGetLastError();
 }
 
