@@ -827,7 +827,7 @@ static_assert(32 * DKDV_NW == kKvKeys, "the split plan counts 256-key dK/dV tile
 // launch of their own between the segments.
 // ------------------------------------------------------------------------------------------
 // SPLIT: some dK/dV tiles run in parts (then the dK/dV run goes first).  A launch without
-// split tiles runs the instance without that code, as compiled before parts existed.
+// split tiles runs the instance compiled without that code, whose loops carry nothing for it.
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(64 * DQ_NW, 2) void k_bwd64(BwdParams pq, BwdParams pk, BwdGrid gr,
                                                          BwdParams pn) {
