@@ -8,7 +8,8 @@ in a graph.  bf16 results come from a fixed schedule, so the checks are bitwise:
   stream;
 - a graph captured from the same four calls (outputs spoiled and accumulators reset by eager
   work between replays) reproduces the eager results on every replay, and so does a graph of
-  the backward entry point that allocates nothing.
+  the backward entry point that allocates nothing, and one whose backward runs long dK/dV key
+  tiles in parts (its graph also holds the launch that adds the parts' sums).
 """
 import numpy as np
 import pytest
@@ -18,6 +19,9 @@ from gpu_helpers import random_inputs, say, to_device
 pytestmark = pytest.mark.gpu
 
 B, S, HQ, HKV, D, BLOCK, KEEP, NSEG = 2, 2048, 8, 2, 128, 64, 0.5, 3
+# one segment of a longer grouped-query problem: its first dK/dV key tiles run in parts, so the
+# captured backward also holds the launch that adds the parts' sums
+SPLIT_SHAPE = dict(B=1, S=8192, HQ=8, HKV=2, KEEP=0.3125, NSEG=1)
 
 
 @pytest.fixture(scope="module")
@@ -31,8 +35,9 @@ def J():
 class Path:
     """Inputs, preallocated outputs and workspaces of one score/select/fwd/bwd pass."""
 
-    def __init__(self, J, seed):
+    def __init__(self, J, seed, B=B, S=S, HQ=HQ, HKV=HKV, KEEP=KEEP, NSEG=NSEG):
         import torch
+        self.KEEP, self.NSEG = KEEP, NSEG
         q, k, v, x0, dout = random_inputs(B, S, HQ, HKV, D, "bf16", seed=seed)
         self.q, self.k, self.v = (to_device(a, "bf16") for a in (q, k, v))
         self.x0 = torch.from_numpy(x0).cuda()
@@ -69,14 +74,14 @@ class Path:
 
     def forward_path(self, J, stream=None):
         J.jenga_score_blocks(self.p, self.q, self.k, self.scores, self.ws_score, stream)
-        J.jenga_select_blocks(self.p, self.scores, J.JENGA_SELECT_TOPK, KEEP, 0, self.kept,
+        J.jenga_select_blocks(self.p, self.scores, J.JENGA_SELECT_TOPK, self.KEEP, 0, self.kept,
                               self.n_kept, stream)
         J.jenga_sparse_attn_fwd(self.p, self.q, self.k, self.v, self.kept, self.n_kept, self.mk,
                                 self.resid, self.o_saved, self.lse, self.ws_fwd, stream)
 
     def backward(self, J, stream=None, noalloc=False):
         args = (self.p, self.q, self.k, self.v, self.kept, self.n_kept, self.mk, self.o_saved,
-                self.lse, self.dout, self.dq, self.dk, self.dv, NSEG)
+                self.lse, self.dout, self.dq, self.dk, self.dv, self.NSEG)
         if noalloc:
             J.jenga_sparse_attn_bwd_segmented_noalloc(*args, stream=stream)
         else:
@@ -119,10 +124,17 @@ def test_path_on_side_stream(J):
     _same(path.outputs(), ref, "side stream")
 
 
-@pytest.mark.parametrize("noalloc", [False, True])
-def test_graph_replays_match_eager(J, noalloc):
+@pytest.mark.parametrize("noalloc,shape", [(False, None), (True, None), (False, "split")])
+def test_graph_replays_match_eager(J, noalloc, shape):
     import torch
-    path = Path(J, seed=505)
+    path = Path(J, seed=505) if shape is None else Path(J, seed=606, **SPLIT_SHAPE)
+    if shape == "split":
+        # one segment of 2560 kept tokens, four query heads per KV head: the first key tiles
+        # run 320 steps, more than the launch's load per compute unit, so they run in parts
+        # and the workspace holds slots beyond the one set of segment buffers
+        L = path.mk * BLOCK
+        one_set = 2 * SPLIT_SHAPE["B"] * SPLIT_SHAPE["HQ"] * L * 4 + 3 * SPLIT_SHAPE["B"] * SPLIT_SHAPE["HQ"] * L * D * 2
+        assert J.workspace_bytes(path.p, J.JENGA_OP_BWD_MIN, path.mk, 1) > one_set
     say(f"eager path (backward {'without' if noalloc else 'with'} a workspace)")
     path.reset()
     path.forward_path(J)
