@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 bf16 flop/clk/CU x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
 KERNELS = ("k_slse64", "k_sblock_mass", "k_eq2_tiles", "k_eq2_reduce", "k_select", "k_pack_tp",
-           "k_fwd64", "k_prep64", "k_bwd64", "k_kv_reduce", "k_proj_gather", "k_proj_scatter",
+           "k_fwd64", "k_fwd_combine", "k_prep64", "k_bwd64", "k_kv_reduce", "k_proj_gather", "k_proj_scatter",
            "k_proj_logits", "k_ce_rows", "k_proj_dh", "k_mlp_act_gated", "k_mlp_block",
            "k_proj_gather_scatter")
 METRIC = "fwd+bwd token-sparse attn TFLOP/s (kept FLOPs) & tokens/s at S=32K; % MFMA peak"

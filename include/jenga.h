@@ -174,6 +174,13 @@ int jenga_select_blocks(const jenga_problem* p, const float* block_scores, int m
  * Rows of eliminated tokens are never read as queries or keys and resid there is not
  * written (bitwise unchanged).
  *
+ * bf16: when a batch row holds few kept tokens for the launch (its longest 128-query tile,
+ * which sees every kept key, would hold more than twice the mean work per workgroup slot), the
+ * row's long query tiles run in parts over ranges of their keys, and a second launch merges
+ * each tile's parts in a fixed order (the online-softmax merge).  The decision follows n_kept
+ * on the device.  Results are deterministic; the partial rows are held in bf16, so a split
+ * tile rounds differently from a single pass, within the bf16 tolerance.
+ *
  *   kept_idx, n_kept   output of jenga_select_blocks (device)
  *   max_kept_blocks    host upper bound on n_kept[b] (1 <= .. <= S/block); sizes the grids
  *                      and the compact outputs; kept blocks beyond it are ignored
@@ -183,8 +190,9 @@ int jenga_select_blocks(const jenga_problem* p, const float* block_scores, int m
  *   lse                [B][Hq][max_kept_blocks*block] fp32, dense, written by kept rank:
  *                      natural-log softmax normaliser of each kept query
  *   workspace          >= jenga_workspace_bytes(p, JENGA_OP_FWD, max_kept_blocks, 1) bytes,
- *                      256-byte aligned (bf16: a transposed copy of the kept V rows; fp32
- *                      needs none and may pass NULL)
+ *                      256-byte aligned (bf16: a transposed copy of the kept V rows, then the
+ *                      part slots of split query tiles, sized for the worst n_kept up to
+ *                      max_kept_blocks; fp32 needs none and may pass NULL)
  */
 int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, const void* v,
                           const int32_t* kept_idx, const int32_t* n_kept, int max_kept_blocks,

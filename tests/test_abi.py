@@ -176,8 +176,36 @@ def test_workspace_scales_with_segments_and_kept_blocks(J):
     assert J.workspace_bytes(pg, J.JENGA_OP_BWD, 90, 1) == one_g         # one segment: one set
     p32 = _problem(J, S=4096, Hq=4, Hkv=4, D=64, block=64, dtype=0)
     assert J.workspace_bytes(p32, J.JENGA_OP_BWD, 32, 4) == J.workspace_bytes(p32, J.JENGA_OP_BWD_MIN, 32, 4)
-    assert J.workspace_bytes(p, J.JENGA_OP_FWD, 128) == vtp
+    slot = 128 * (2 * 128 + 8)                    # a query tile's bf16 rows, fp32 max and sum
+    assert J.workspace_bytes(p, J.JENGA_OP_FWD, 128) == vtp + 32 * 27 * slot
     assert J.workspace_bytes(_problem(J), J.JENGA_OP_FWD, 8) == 0       # fp32 path needs none
+
+
+def test_fwd_workspace_part_slots(J):
+    # A batch row of n 128-query tiles splits when (n + 1) * Hq * B < 768 (its longest tile, 4n
+    # steps of 32 keys, is more than twice the mean 2n(n + 1) Hq B / 768 per workgroup slot);
+    # parts are T = max(32, ceil(mean)) steps, and only tiles longer than T take slots.  The
+    # workspace holds the worst row up to the capacity.
+    slot = lambda D: 128 * (2 * D + 8)            # 128 unnormalised bf16 rows, fp32 max and sum
+    vtp = lambda B, Hkv, ncap, D: B * Hkv * ncap * D * 2
+    # 32 heads, capacity 16384: rows of n <= 22 tiles split; the most slots are at n = 20
+    # (T = 26880 / 768 = 35): tiles 8..16 (36..68 steps) in 2 parts, 17..19 (72..80) in 3
+    c5 = _problem(J, S=32768, Hq=32, Hkv=32, D=128, block=128, dtype=1)
+    assert J.workspace_bytes(c5, J.JENGA_OP_FWD, 128) == vtp(1, 32, 16384, 128) + 32 * 27 * slot(128)
+    # capacity 2048 (n <= 16, T = 32): tiles 8..15 (36..64 steps) in 2 parts
+    c2 = _problem(J, S=4096, Hq=32, Hkv=32, D=128, block=64, dtype=1)
+    assert J.workspace_bytes(c2, J.JENGA_OP_FWD, 32) == vtp(1, 32, 2048, 128) + 32 * 16 * slot(128)
+    # capacity 1024: no tile is longer than 32 steps, nothing splits
+    assert J.workspace_bytes(c2, J.JENGA_OP_FWD, 16) == vtp(1, 32, 1024, 128)
+    # 64 heads x 2 rows: (n + 1) * 128 < 768 leaves n <= 4, tiles of at most 16 steps
+    wide = _problem(J, B=2, S=4096, Hq=64, Hkv=8, D=64, block=64, dtype=1)
+    assert J.workspace_bytes(wide, J.JENGA_OP_FWD, 64) == vtp(2, 8, 4096, 64)
+    # whatever the shape, a (row, head) takes fewer than 1536 / (Hq B) slots
+    for B, Hq, S, D in ((1, 1, 65536, 64), (1, 2, 32768, 128), (2, 4, 16384, 64), (1, 8, 16384, 128)):
+        pr = _problem(J, B=B, S=S, Hq=Hq, Hkv=1, D=D, block=64, dtype=1)
+        extra = J.workspace_bytes(pr, J.JENGA_OP_FWD, S // 64) - vtp(B, 1, S, D)
+        assert extra % (B * Hq * slot(D)) == 0
+        assert 0 < extra // (B * Hq * slot(D)) < 1536 // (B * Hq)
 
 
 def test_score_workspace(J):

@@ -172,6 +172,51 @@ def test_fwd_bwd(J, B, S, Hq, Hkv, D, block, dtype, kept, nseg):
             assert np.all(got[b, elim] == 0), name
 
 
+# Forward over few kept tokens: a row's query tiles of more than 32 key steps run in parts
+# merged by k_fwd_combine.  Row 0 below keeps 40 blocks of 64 (20 tiles of 128 queries: tiles
+# 8..19 split, the last in 3 parts); row 1 keeps 9 blocks (5 tiles, none longer than a part);
+# the D=64 case keeps 15 of 16 blocks of 128 with a capacity of 16 blocks (a short last tile).
+SPLIT_FWD_CASES = [
+    # B, S, Hq, Hkv, D, block, kept counts, capacity (blocks)
+    (2, 4096, 4, 2, 128, 64, (40, 9), 40),
+    (1, 2048, 2, 2, 64, 128, (15,), 16),
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,block,counts,maxk", SPLIT_FWD_CASES)
+def test_fwd_split_tiles(J, B, S, Hq, Hkv, D, block, counts, maxk):
+    nkb = S // block
+    rng = np.random.default_rng(sum(counts) + D)
+    kept = [np.sort(rng.choice(nkb, c, replace=False)) for c in counts]
+    q, k, v, x0, dout = random_inputs(B, S, Hq, Hkv, D, "bf16", seed=31 + D)
+    say(f"split forward B{B} S{S} Hq{Hq} Hkv{Hkv} D{D} block{block} kept {counts} cap {maxk}")
+    first = _run_attn(J, q, k, v, x0, dout, kept, block, "bf16", 2, maxk=maxk)
+    again = _run_attn(J, q, k, v, x0, dout, kept, block, "bf16", 2, maxk=maxk)
+    # parts merge in a fixed order: bitwise repeatable (o_saved and lse rows past a batch row's
+    # kept count are not written)
+    for i in (0, 3, 4, 5):
+        assert np.array_equal(first[i], again[i])
+    for b, c in enumerate(counts):
+        n = c * block
+        assert np.array_equal(first[1][b, :n], again[1][b, :n])
+        assert np.array_equal(first[2][b, :, :n], again[2][b, :, :n])
+    resid, o_saved, lse, dq, dk, dv = first
+    tol = tol_for("bf16")
+    O, LSE = oracle.attn_fwd(q, k, v, kept, block)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, kept, block, dout)
+    for b in range(B):
+        pos = oracle.token_positions(kept[b], block)
+        elim = np.setdiff1d(np.arange(S), pos)
+        assert np.array_equal(resid[b, elim], x0[b, elim])
+        assert max_abs(resid[b, pos] - x0[b, pos], O[b, pos]) <= tol
+        assert max_abs(o_saved[b, :len(pos)], O[b, pos]) <= tol
+        lr = lse[b][:, :len(pos)]
+        assert np.max(np.abs(lr - LSE[b][:, pos]) / np.maximum(1.0, np.abs(LSE[b][:, pos]))) <= 1e-5
+        for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            err = max_abs(got[b, pos], ref[b, pos])
+            assert err <= tol * max(1.0, float(np.max(np.abs(ref[b, pos])))), (b, name, err)
+
+
 def test_bwd_segments_equivalent(J):
     """N = 1 and N = 8 segments give the same gradients up to fp32 rounding."""
     B, S, Hq, Hkv, D, block, dtype = 1, 2048, 4, 4, 128, 128, "bf16"

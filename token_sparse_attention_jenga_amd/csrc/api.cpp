@@ -156,9 +156,23 @@ size_t bwd_ws_bytes(const jenga_problem* p, int max_kept_blocks, int n_segments)
   return (two ? 2 * one : one) + bwd_kv_slot_bytes(p, max_kept_blocks, n_segments);
 }
 
+// bf16 forward: the TP tiles of the kept V rows, then the part slots of split query tiles
+size_t fwd_vtp_bytes(const jenga_problem* p, int max_kept_blocks) {
+  return align_up((size_t)p->batch * p->n_heads_kv * max_kept_blocks * p->block * p->head_dim * 2);
+}
+
+int fwd_slots(const jenga_problem* p, int max_kept_blocks) {
+  int items, slots, split_tiles;
+  jenga::fwd_split_bounds(max_kept_blocks * p->block, p->n_heads_q, p->batch, &items, &slots,
+                          &split_tiles);
+  return slots;
+}
+
 size_t fwd_ws_bytes(const jenga_problem* p, int max_kept_blocks) {
   if (p->dtype != JENGA_DTYPE_BF16) return 0;
-  return align_up((size_t)p->batch * p->n_heads_kv * max_kept_blocks * p->block * p->head_dim * 2);
+  const size_t slot = (size_t)jenga::kFwdRows * (2 * p->head_dim + 8);   // bf16 rows, fp32 m, l
+  return fwd_vtp_bytes(p, max_kept_blocks) +
+         align_up((size_t)p->batch * p->n_heads_q * fwd_slots(p, max_kept_blocks) * slot);
 }
 
 size_t score_eq2_ws_bytes(const jenga_problem* p) {
@@ -467,6 +481,12 @@ int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, 
   fp.ncap = max_kept_blocks * p->block;
   fp.scale_log2 = scale_of(p) * 1.4426950408889634f;
   fp.vtp = workspace;
+  fp.wsPart = nullptr;
+  fp.fs_slots = 0;
+  if (p->dtype == JENGA_DTYPE_BF16) {
+    fp.wsPart = (char*)workspace + fwd_vtp_bytes(p, max_kept_blocks);
+    fp.fs_slots = fwd_slots(p, max_kept_blocks);
+  }
   const hipError_t e = p->dtype == JENGA_DTYPE_BF16
                            ? jenga::launch_fwd64(fp, p->head_dim, (hipStream_t)stream)
                            : jenga::launch_fwd_f32(fp, (hipStream_t)stream);

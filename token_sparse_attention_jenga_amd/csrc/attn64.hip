@@ -12,7 +12,9 @@
 // the natural K tile (see tiles64.h).
 //
 //   k_pack_tp   kept rows of V (head h) -> TP tiles [D][32] in a workspace (forward)
-//   k_fwd64     forward:   S^T = K Q^T, online softmax per query (lane-local), O^T += V^T P^T
+//   k_fwd64     forward:   S^T = K Q^T, online softmax per query (lane-local), O^T += V^T P^T;
+//               rows with few kept tokens run their long query tiles in parts over key ranges
+//   k_fwd_combine  after a forward with split tiles: merges each tile's parts in part order
 //   k_prep64    backward prologue per segment: D_i = dO_i.O_i, dOut -> bf16 natural + TP,
 //               the segment's Q rows -> TP
 //   k_bwd64     one launch per segment with two kinds of workgroup tiles (no atomics):
@@ -95,7 +97,10 @@ static hipError_t pack_tp(const PackArgs& a, int B, hipStream_t st) {
 // bf16 range, and the final normalisation uses the same stale max, so the result is exact.
 constexpr float kLazyRescale = 8.f;
 
-template <int D, int NB, int NW>
+// SPLIT: the instance for launches where some batch row's long query tiles run in parts (see
+// fwd_row_splits); workgroup x of a (head, batch row) then takes the row's tiles heaviest first
+// and each tile as its parts.  Without it, workgroup x takes tile nqt - 1 - x.
+template <int D, int NB, int NW, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p) {
   constexpr int RW = 32 * NB, RG = RW * NW;                // rows per wave / per workgroup
   using C = T64<D>;
@@ -115,12 +120,35 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
   const int32_t* kept = p.kept + (int64_t)b * p.nkb;
   const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
   const int nqt = (Nk + RG - 1) / RG;
-  if (tl.x >= nqt) return;
-  const int q0 = (nqt - 1 - tl.x) * RG;                  // heaviest tiles first
+  int tile, part = 0, nparts = 1, sbase = 0;             // slots of the row's earlier split tiles
+  if (SPLIT && fwd_row_splits(nqt, p.Hq * p.B)) {
+    static_assert(!SPLIT || RG == kFwdRows, "the split plan counts 128-query tiles");
+    const int T = fwd_part_steps(nqt, p.Hq * p.B);
+    int rem = tl.x;
+    for (tile = nqt - 1;; --tile) {                      // heaviest tiles first, each as its parts
+      if (tile < 0) return;
+      nparts = fwd_tile_parts(fwd_tile_steps(tile, Nk), T);
+      if (rem < nparts) break;
+      rem -= nparts;
+    }
+    part = rem;
+    if (nparts > 1)
+      for (int u = 0; u < tile; ++u) {
+        const int k = fwd_tile_parts(fwd_tile_steps(u, Nk), T);
+        if (k > 1) sbase += k;
+      }
+  } else {
+    if (tl.x >= nqt) return;
+    tile = nqt - 1 - tl.x;                               // heaviest tiles first
+  }
+  const int q0 = tile * RG;
   const int qw0 = q0 + RW * w;
   const bool active = qw0 < Nk;                          // Nk is a multiple of 64 >= RW
   const int qlast = min(q0 + RG, Nk) - 1;
-  const int nsteps = qlast / 32 + 1;
+  const int tsteps = qlast / 32 + 1;
+  // this part's key steps: an equal share of the tile's (the whole tile when not split)
+  const int s0 = part * tsteps / nparts;
+  const int nsteps = (part + 1) * tsteps / nparts - s0;
   stage_kept(ktab, kept, qlast / p.block + 1);
   __syncthreads();
   const KeptTab kt{(const LDS_AS int*)ktab, kept, p.block};
@@ -242,15 +270,41 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
     if (!DC::EXACT) wait_all_mem();
     else wait_vm<PER>();
     stage_barrier();
-    issue(min(t + 2, nsteps - 1), nxt);
-    compute(t, cur);
+    issue(s0 + min(t + 2, nsteps - 1), nxt);
+    compute(s0 + t, cur);
   };
-  issue(0, sA);
-  issue(min(1, nsteps - 1), sB);
+  issue(s0, sA);
+  issue(s0 + min(1, nsteps - 1), sB);
   ring3_loop(nsteps, sA, sB, sC, stage);
   wait_all_mem();                                        // drain the trailing reloads
 
   if (!active) return;
+  if (SPLIT && nparts > 1) {
+    // a part of a split tile: its unnormalised rows, running max (the reference the rows were
+    // scaled by) and sum go to its slot; a wave whose rows precede the part's keys writes zero
+    // rows, max -inf and sum 0, which the merge weights by exp2(-inf) = 0
+    char* so = p.wsPart + (((int64_t)b * p.Hq + h) * p.fs_slots + sbase + part) * FwdSlot<D>::BYTES;
+    float* sml = (float*)(so + FwdSlot<D>::O_BYTES);
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      const int r = RW * w + 32 * qb + lc;               // row within the tile
+      const float lsum = half_pair_sum(l_run[qb]);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          u32x2 pw;
+          pw[0] = pack_bf16x2(o[qb][db][4 * rg + 0], o[qb][db][4 * rg + 1]);
+          pw[1] = pack_bf16x2(o[qb][db][4 * rg + 2], o[qb][db][4 * rg + 3]);
+          *(u32x2*)(so + (r * D + db * 32 + 8 * rg + 4 * hl) * 2) = pw;
+        }
+      if (hl == 0) {
+        sml[r] = m_run[qb];
+        sml[RG + r] = lsum;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < NB; ++qb) {
     const int qr = qw0 + 32 * qb + lc;
@@ -283,6 +337,132 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
       }
     }
     if (hl == 0) p.lse[((int64_t)b * p.Hq + h) * p.ncap + qr] = (m_run[qb] + log2f(lsum)) * kLn2;
+  }
+}
+
+// Merge of a split query tile's parts.  Workgroup x of a (head, batch row) takes 32 rows of the
+// row's split tile x / 4 (split tiles counted from the first); a thread takes 4 columns of
+// 32 / ROWS of those rows, ROWS apart.  A row's parts, with running maxima m_p, sums l_p and
+// unnormalised rows O_p, combine as
+//   M = max_p m_p,  w_p = exp2(m_p - M),  L = sum_p w_p l_p,  O = (sum_p w_p O_p) / L,
+// the online-softmax merge, added in part order.  The row then goes out as the whole tile's
+// epilogue writes it: resid += O, o_saved = bf16(O), lse = (M + log2 L) ln 2.  A thread's loads
+// for all its rows go out together (rows past the kept count load row 0 of the tile and store
+// nothing), four parts at a time; the merge is latency-bound, not bandwidth-bound.
+template <int D>
+struct Combine {
+  static constexpr int C4 = D / 4;                  // 4-column chunks per row
+  static constexpr int ROWS = 256 / C4;             // rows a workgroup covers at once
+  static constexpr int PER = 32 / ROWS;             // rows per thread
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void k_fwd_combine(FwdParams p) {
+  constexpr int RG = kFwdRows, C4 = Combine<D>::C4, ROWS = Combine<D>::ROWS, PER = Combine<D>::PER;
+  constexpr int64_t SLOT = FwdSlot<D>::BYTES, OB = FwdSlot<D>::O_BYTES;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int Nk = min(p.n_kept[b], p.max_kept_blocks) * p.block;
+  const int nqt = (Nk + RG - 1) / RG;
+  if (!fwd_row_splits(nqt, p.Hq * p.B)) return;
+  const int T = fwd_part_steps(nqt, p.Hq * p.B);
+  int tile = 0, sbase = 0, nparts = 1;
+  for (int j = blockIdx.x >> 2;; ++tile) {
+    if (tile >= nqt) return;
+    nparts = fwd_tile_parts(fwd_tile_steps(tile, Nk), T);
+    if (nparts > 1) {
+      if (j == 0) break;
+      --j;
+      sbase += nparts;
+    }
+  }
+  const int q0 = tile * RG;
+  const int c = (int)threadIdx.x % C4;
+  int r[PER];
+  bool valid[PER];
+  int kb[PER];
+  const int32_t* kept = p.kept + (int64_t)b * p.nkb;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int rr = (blockIdx.x & 3) * 32 + (int)threadIdx.x / C4 + ROWS * i;
+    valid[i] = q0 + rr < Nk;
+    r[i] = valid[i] ? rr : 0;
+    kb[i] = kept[(q0 + r[i]) / p.block];
+  }
+  const char* sl = p.wsPart + (((int64_t)b * p.Hq + h) * p.fs_slots + sbase) * SLOT;
+  float M[PER], L[PER];
+  f32x4 acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    M[i] = -INFINITY;
+    L[i] = 0.f;
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // four parts at a time; across groups of four the sums are rescaled to the new maximum as in
+  // the online softmax (one group for up to four parts)
+  for (int k0 = 0; k0 < nparts; k0 += 4) {
+    const int nk = min(4, nparts - k0);
+    float m[PER][4], l[PER][4];
+    u32x2 o[PER][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const char* pk = sl + (k0 + min(k, nk - 1)) * SLOT;   // absent parts reload the last
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        m[i][k] = ((const float*)(pk + OB))[r[i]];
+        l[i][k] = ((const float*)(pk + OB))[RG + r[i]];
+        o[i][k] = *(const u32x2*)(pk + (r[i] * D + 4 * c) * 2);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      float Mn = M[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k < nk) Mn = fmaxf(Mn, m[i][k]);
+      const float sc = __builtin_amdgcn_exp2f(M[i] - Mn);   // 0 for the first group (M = -inf)
+      L[i] *= sc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][e] *= sc;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (k < nk) {
+          const float wk = __builtin_amdgcn_exp2f(m[i][k] - Mn);
+          L[i] += wk * l[i][k];
+          acc[i][0] += wk * bf16_lo(o[i][k][0]);
+          acc[i][1] += wk * bf16_hi(o[i][k][0]);
+          acc[i][2] += wk * bf16_lo(o[i][k][1]);
+          acc[i][3] += wk * bf16_hi(o[i][k][1]);
+        }
+      }
+      M[i] = Mn;
+    }
+  }
+  float* rrow[PER];
+  f32x4 x[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int qr = q0 + r[i];
+    const int pos = kb[i] * p.block + (qr - (qr / p.block) * p.block);
+    rrow[i] = p.resid + (((int64_t)b * p.S + pos) * p.Hq + h) * D + 4 * c;
+    x[i] = *(const f32x4*)rrow[i];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (!valid[i]) continue;
+    const int qr = q0 + r[i];
+    const float inv = 1.f / L[i];
+    const float v0 = acc[i][0] * inv, v1 = acc[i][1] * inv, v2 = acc[i][2] * inv, v3 = acc[i][3] * inv;
+    f32x4 y = x[i];
+    y[0] += v0;
+    y[1] += v1;
+    y[2] += v2;
+    y[3] += v3;
+    *(f32x4*)rrow[i] = y;
+    u32x2 pw;
+    pw[0] = pack_bf16x2(v0, v1);
+    pw[1] = pack_bf16x2(v2, v3);
+    *(u32x2*)((char*)p.o_saved + ((((int64_t)b * p.ncap + qr) * p.Hq + h) * D + 4 * c) * 2) = pw;
+    if (c == 0) p.lse[((int64_t)b * p.Hq + h) * p.ncap + qr] = (M[i] + log2f(L[i])) * kLn2;
   }
 }
 
@@ -997,10 +1177,48 @@ static hipError_t launch_fwd64_t(const FwdParams& p, hipStream_t st) {
              0, p.ncap, p.ncap / 32, p.Hkv, p.vtp};
   hipError_t e = pack_tp<D>(a, p.B, st);
   if (e != hipSuccess) return e;
-  constexpr int RG = 32 * FWD_NB * FWD_NW;
-  TimedLaunch tl("k_fwd64", st);
-  k_fwd64<D, FWD_NB, FWD_NW><<<dim3((p.ncap + RG - 1) / RG, p.Hq, p.B), 64 * FWD_NW, 0, st>>>(p);
+  static_assert(32 * FWD_NB * FWD_NW == kFwdRows, "forward query tiles are 128 rows");
+  int items, slots, split_tiles;
+  fwd_split_bounds(p.ncap, p.Hq, p.B, &items, &slots, &split_tiles);
+  if (slots == 0 || p.fs_slots < slots) {
+    TimedLaunch tl("k_fwd64", st);
+    k_fwd64<D, FWD_NB, FWD_NW, false><<<dim3(items, p.Hq, p.B), 64 * FWD_NW, 0, st>>>(p);
+    return hipGetLastError();
+  }
+  {
+    TimedLaunch tl("k_fwd64", st);
+    k_fwd64<D, FWD_NB, FWD_NW, true><<<dim3(items, p.Hq, p.B), 64 * FWD_NW, 0, st>>>(p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  TimedLaunch tl("k_fwd_combine", st);
+  k_fwd_combine<D><<<dim3(4 * split_tiles, p.Hq, p.B), 256, 0, st>>>(p);
   return hipGetLastError();
+}
+
+void fwd_split_bounds(int ncap, int Hq, int B, int* items, int* slots, int* split_tiles) {
+  const int ntc = (ncap + kFwdRows - 1) / kFwdRows;
+  int it_max = ntc, sl_max = 0, st_max = 0;
+  // a row of n tiles (its last one possibly short) needs no more than a row of n full tiles;
+  // rows that split are those of few tiles, so the loop ends early
+  for (int n = 1; n <= ntc && fwd_row_splits(n, Hq * B); ++n) {
+    const int T = fwd_part_steps(n, Hq * B);
+    int it = 0, sl = 0, st = 0;
+    for (int t = 0; t < n; ++t) {
+      const int k = fwd_tile_parts(fwd_tile_steps(t, n * kFwdRows), T);
+      it += k;
+      if (k > 1) {
+        sl += k;
+        ++st;
+      }
+    }
+    it_max = max(it_max, it);
+    sl_max = max(sl_max, sl);
+    st_max = max(st_max, st);
+  }
+  *items = it_max;
+  *slots = sl_max;
+  *split_tiles = st_max;
 }
 
 hipError_t launch_fwd64(const FwdParams& p, int D, hipStream_t st) {

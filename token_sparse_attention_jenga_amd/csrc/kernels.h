@@ -84,9 +84,59 @@ struct FwdParams {
   void* o_saved;
   float* lse;
   void* vtp;     // bf16 path: workspace [B][Hkv][ncap/32] TP tiles of the kept V rows
+  char* wsPart;  // bf16 path: [B][Hq][fs_slots] slots of split query tiles' parts (FwdSlot)
   int B, S, Hq, Hkv, block, nkb, max_kept_blocks, ncap;
   float scale_log2;
+  int fs_slots;  // part slots per (batch row, query head); 0: no query tile is split
 };
+
+// A causal forward over few kept tokens lasts as long as its longest query tile, the last one,
+// whose queries see every kept key.  When a batch row's longest tile holds more than twice the
+// mean work per workgroup slot of the launch, the row's tiles longer than a part run in parts
+// over equal ranges of their key steps.  Each part writes its unnormalised output rows and their
+// running max and sum to a slot; k_fwd_combine merges a tile's parts in part order (a fixed
+// order) and writes the residual, o_saved and lse as the whole tile would.  The plan follows each
+// row's own kept count (read on the device), so no host synchronisation is needed; the host
+// sizes the grid and the slots for the worst count up to the capacity.  A query tile is 128
+// kept queries, a step 32 kept keys; three workgroups share a compute unit.
+constexpr int kFwdRows = 128;
+constexpr int kFwdWgPerCu = 3;
+constexpr int kFwdMinPartSteps = 32;
+
+// key steps of query tile t of a batch row with nk kept ranks (nk > t * kFwdRows)
+__host__ __device__ inline int fwd_tile_steps(int t, int nk) {
+  const int end = (t + 1) * kFwdRows < nk ? (t + 1) * kFwdRows : nk;
+  return (end - 1) / 32 + 1;
+}
+// Whether a row of ntiles query tiles splits, with HqB = query heads x batch rows workgroups per
+// tile index (every row taken to be alike).  Its tiles hold 2 ntiles (ntiles + 1) steps, so the
+// mean per workgroup slot is 2 ntiles (ntiles + 1) HqB / (256 kFwdWgPerCu); the longest tile,
+// 4 ntiles steps, exceeds twice that exactly when (ntiles + 1) HqB < 256 kFwdWgPerCu.
+__host__ __device__ inline bool fwd_row_splits(int ntiles, int HqB) {
+  return (long long)(ntiles + 1) * HqB < 256 * kFwdWgPerCu;
+}
+// Steps per part: that mean, and no fewer than kFwdMinPartSteps.  Since a tile longer than a part
+// of T steps makes ceil(s / T) <= 2 s / T parts, a row's slots stay below 4 ntiles (ntiles + 1) / T
+// <= 2 * 256 kFwdWgPerCu / HqB, whatever the shape.
+__host__ __device__ inline int fwd_part_steps(int ntiles, int HqB) {
+  const long long slots = 256 * kFwdWgPerCu;
+  const long long mean = (2LL * ntiles * (ntiles + 1) * HqB + slots - 1) / slots;
+  return mean > kFwdMinPartSteps ? (int)mean : kFwdMinPartSteps;
+}
+__host__ __device__ inline int fwd_tile_parts(int steps, int part_steps) {
+  return (steps + part_steps - 1) / part_steps;
+}
+// A part's slot: its 128 unnormalised output rows in bf16 (D values each), then the rows'
+// running maxima and sums in fp32.  bf16 rows halve the slot traffic, which a merge pays on top
+// of the unsplit tile's; they round as the P operand of the P V product already did.
+template <int D>
+struct FwdSlot {
+  static constexpr int64_t O_BYTES = (int64_t)kFwdRows * D * 2;
+  static constexpr int64_t BYTES = O_BYTES + (int64_t)kFwdRows * 8;
+};
+// Worst case over the kept counts up to ncap: workgroups per (batch row, query head) of the
+// forward launch, part slots and split tiles per (batch row, query head).
+void fwd_split_bounds(int ncap, int Hq, int B, int* items, int* slots, int* split_tiles);
 
 struct BwdParams {
   const void* q;
