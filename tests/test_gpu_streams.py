@@ -9,7 +9,8 @@ in a graph.  bf16 results come from a fixed schedule, so the checks are bitwise:
 - a graph captured from the same four calls (outputs spoiled and accumulators reset by eager
   work between replays) reproduces the eager results on every replay, and so does a graph of
   the backward entry point that allocates nothing, and one whose backward runs long dK/dV key
-  tiles in parts (its graph also holds the launch that adds the parts' sums).
+  tiles in parts and whose forward runs long query tiles in parts (its graph also holds the
+  launches that add and merge the parts).
 """
 import numpy as np
 import pytest
