@@ -161,18 +161,21 @@ size_t fwd_vtp_bytes(const jenga_problem* p, int max_kept_blocks) {
   return align_up((size_t)p->batch * p->n_heads_kv * max_kept_blocks * p->block * p->head_dim * 2);
 }
 
-int fwd_slots(const jenga_problem* p, int max_kept_blocks) {
+struct FwdPlan {
   int items, slots, split_tiles;
-  jenga::fwd_split_bounds(max_kept_blocks * p->block, p->n_heads_q, p->batch, &items, &slots,
-                          &split_tiles);
-  return slots;
+};
+
+FwdPlan fwd_plan(const jenga_problem* p, int max_kept_blocks) {
+  FwdPlan f;
+  jenga::fwd_split_bounds(max_kept_blocks * p->block, p->n_heads_q, p->batch, &f.items, &f.slots,
+                          &f.split_tiles);
+  return f;
 }
 
-size_t fwd_ws_bytes(const jenga_problem* p, int max_kept_blocks) {
+size_t fwd_ws_bytes(const jenga_problem* p, int max_kept_blocks, const FwdPlan& f) {
   if (p->dtype != JENGA_DTYPE_BF16) return 0;
   const size_t slot = (size_t)jenga::kFwdRows * (2 * p->head_dim + 8);   // bf16 rows, fp32 m, l
-  return fwd_vtp_bytes(p, max_kept_blocks) +
-         align_up((size_t)p->batch * p->n_heads_q * fwd_slots(p, max_kept_blocks) * slot);
+  return fwd_vtp_bytes(p, max_kept_blocks) + align_up((size_t)p->batch * p->n_heads_q * f.slots * slot);
 }
 
 size_t score_eq2_ws_bytes(const jenga_problem* p) {
@@ -340,7 +343,7 @@ size_t jenga_workspace_bytes(const jenga_problem* p, int op, int max_kept_blocks
   if (op == JENGA_OP_FWD) {
     const int nkb = p->seq_len / p->block;
     if (max_kept_blocks < 1 || max_kept_blocks > nkb) return 0;
-    return fwd_ws_bytes(p, max_kept_blocks);
+    return fwd_ws_bytes(p, max_kept_blocks, fwd_plan(p, max_kept_blocks));
   }
   if (op == JENGA_OP_BWD || op == JENGA_OP_BWD_MIN) {
     const int nkb = p->seq_len / p->block;
@@ -456,7 +459,8 @@ int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(resid) || !aligned16(o_saved))
     return JENGA_ERR_INVALID_ARG;
   if (max_kept_blocks < 1 || max_kept_blocks > nkb) return JENGA_ERR_INVALID_ARG;
-  const size_t need = fwd_ws_bytes(p, max_kept_blocks);
+  const FwdPlan plan = fwd_plan(p, max_kept_blocks);
+  const size_t need = fwd_ws_bytes(p, max_kept_blocks, plan);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0))
     return JENGA_ERR_WORKSPACE;
   jenga::FwdParams fp;
@@ -482,10 +486,12 @@ int jenga_sparse_attn_fwd(const jenga_problem* p, const void* q, const void* k, 
   fp.scale_log2 = scale_of(p) * 1.4426950408889634f;
   fp.vtp = workspace;
   fp.wsPart = nullptr;
+  fp.fs_items = plan.items;
   fp.fs_slots = 0;
+  fp.fs_split_tiles = plan.split_tiles;
   if (p->dtype == JENGA_DTYPE_BF16) {
     fp.wsPart = (char*)workspace + fwd_vtp_bytes(p, max_kept_blocks);
-    fp.fs_slots = fwd_slots(p, max_kept_blocks);
+    fp.fs_slots = plan.slots;
   }
   const hipError_t e = p->dtype == JENGA_DTYPE_BF16
                            ? jenga::launch_fwd64(fp, p->head_dim, (hipStream_t)stream)

@@ -1178,38 +1178,40 @@ static hipError_t launch_fwd64_t(const FwdParams& p, hipStream_t st) {
   hipError_t e = pack_tp<D>(a, p.B, st);
   if (e != hipSuccess) return e;
   static_assert(32 * FWD_NB * FWD_NW == kFwdRows, "forward query tiles are 128 rows");
-  int items, slots, split_tiles;
-  fwd_split_bounds(p.ncap, p.Hq, p.B, &items, &slots, &split_tiles);
-  if (slots == 0 || p.fs_slots < slots) {
+  if (p.fs_slots == 0) {
     TimedLaunch tl("k_fwd64", st);
-    k_fwd64<D, FWD_NB, FWD_NW, false><<<dim3(items, p.Hq, p.B), 64 * FWD_NW, 0, st>>>(p);
+    k_fwd64<D, FWD_NB, FWD_NW, false><<<dim3((p.ncap + kFwdRows - 1) / kFwdRows, p.Hq, p.B),
+                                         64 * FWD_NW, 0, st>>>(p);
     return hipGetLastError();
   }
   {
     TimedLaunch tl("k_fwd64", st);
-    k_fwd64<D, FWD_NB, FWD_NW, true><<<dim3(items, p.Hq, p.B), 64 * FWD_NW, 0, st>>>(p);
+    k_fwd64<D, FWD_NB, FWD_NW, true><<<dim3(p.fs_items, p.Hq, p.B), 64 * FWD_NW, 0, st>>>(p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   TimedLaunch tl("k_fwd_combine", st);
-  k_fwd_combine<D><<<dim3(4 * split_tiles, p.Hq, p.B), 256, 0, st>>>(p);
+  k_fwd_combine<D><<<dim3(4 * p.fs_split_tiles, p.Hq, p.B), 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
 void fwd_split_bounds(int ncap, int Hq, int B, int* items, int* slots, int* split_tiles) {
   const int ntc = (ncap + kFwdRows - 1) / kFwdRows;
   int it_max = ntc, sl_max = 0, st_max = 0;
-  // a row of n tiles (its last one possibly short) needs no more than a row of n full tiles;
-  // rows that split are those of few tiles, so the loop ends early
+  // A row of n tiles (its last one possibly short) needs no more than a row of n full tiles,
+  // whose tile j = 1..n holds 4j steps and makes k = ceil(4j / T) parts; the tiles of one k are
+  // those with (k - 1) T < 4j <= k T, counted at once.  Rows that split are those of few tiles,
+  // so the loop over n ends early.
   for (int n = 1; n <= ntc && fwd_row_splits(n, Hq * B); ++n) {
     const int T = fwd_part_steps(n, Hq * B);
     int it = 0, sl = 0, st = 0;
-    for (int t = 0; t < n; ++t) {
-      const int k = fwd_tile_parts(fwd_tile_steps(t, n * kFwdRows), T);
-      it += k;
+    for (int k = 1; (k - 1) * T < 4 * n; ++k) {
+      const int jlo = (k - 1) * T / 4 + 1, jhi = min(n, k * T / 4);
+      const int c = max(0, jhi - jlo + 1);
+      it += k * c;
       if (k > 1) {
-        sl += k;
-        ++st;
+        sl += k * c;
+        st += c;
       }
     }
     it_max = max(it_max, it);

@@ -87,7 +87,10 @@ struct FwdParams {
   char* wsPart;  // bf16 path: [B][Hq][fs_slots] slots of split query tiles' parts (FwdSlot)
   int B, S, Hq, Hkv, block, nkb, max_kept_blocks, ncap;
   float scale_log2;
-  int fs_slots;  // part slots per (batch row, query head); 0: no query tile is split
+  // the split plan's bounds (fwd_split_bounds) for ncap, Hq, B
+  int fs_items;        // workgroups per (batch row, query head) of the forward launch
+  int fs_slots;        // part slots per (batch row, query head); 0: no query tile is split
+  int fs_split_tiles;  // split tiles per (batch row, query head)
 };
 
 // A causal forward over few kept tokens lasts as long as its longest query tile, the last one,
