@@ -175,11 +175,14 @@ def test_fwd_bwd(J, B, S, Hq, Hkv, D, block, dtype, kept, nseg):
 # Forward over few kept tokens: a row's query tiles of more than 32 key steps run in parts
 # merged by k_fwd_combine.  Row 0 below keeps 40 blocks of 64 (20 tiles of 128 queries: tiles
 # 8..19 split, the last in 3 parts); row 1 keeps 9 blocks (5 tiles, none longer than a part);
-# the D=64 case keeps 15 of 16 blocks of 128 with a capacity of 16 blocks (a short last tile).
+# the D=64 case keeps 15 of 16 blocks of 128 with a capacity of 16 blocks; the last case keeps
+# 37 blocks of 64, so its last tile holds 64 queries (two of its four waves idle) and runs 74
+# steps in 3 parts, with two query heads on one KV head.
 SPLIT_FWD_CASES = [
     # B, S, Hq, Hkv, D, block, kept counts, capacity (blocks)
     (2, 4096, 4, 2, 128, 64, (40, 9), 40),
     (1, 2048, 2, 2, 64, 128, (15,), 16),
+    (1, 4096, 2, 1, 128, 64, (37,), 48),
 ]
 
 
