@@ -96,12 +96,13 @@ static hipError_t pack_tp(const PackArgs& a, int B, hipStream_t st) {
 // kLazyRescale (log2 units): exp2(z - m) then stays below 2^kLazyRescale, far inside fp32 and
 // bf16 range, and the final normalisation uses the same stale max, so the result is exact.
 constexpr float kLazyRescale = 8.f;
+constexpr float kLazyCheck = 128.f;    // 2^7: a lane sum above it may need the rule
 
 // SPLIT: the instance for launches where some batch row's long query tiles run in parts (see
 // fwd_row_splits); workgroup x of a (head, batch row) then takes the row's tiles heaviest first
 // and each tile as its parts.  Without it, workgroup x takes tile nqt - 1 - x.
 template <int D, int NB, int NW, bool SPLIT>
-__global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p) {
+__global__ __launch_bounds__(64 * NW, NB == 1 ? 3 : 1) void k_fwd64(FwdParams p) {
   constexpr int RW = 32 * NB, RG = RW * NW;                // rows per wave / per workgroup
   using C = T64<D>;
   constexpr int OFF_V = C::NAT32;
@@ -222,30 +223,42 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void k_fwd64(FwdParams p)
         for (int r = 0; r < 16; ++r)
           if (8 * (r >> 2) + (r & 3) > lim) st[qb][r] = -INFINITY;
       }
-      const float mx = half_pair_max(max16(st[qb])) * c2;  // row max in the log2 domain
-      // lazy rescale: move the reference max only when it grows by kLazyRescale or more
-      const bool grow = mx > m_run[qb] + kLazyRescale;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = fmaxf(m_run[qb], mx);
-        float dm = m_run[qb] - m_new;
-        // keep the rescale factor's exponential inside the branch: left alone, the compiler
-        // computes it on every step, one quarter-rate instruction per step for nothing
-        asm volatile("" : "+v"(dm));
-        const float alpha = __builtin_amdgcn_exp2f(dm);
-        l_run[qb] *= alpha;
-        m_run[qb] = m_new;
+      // P against the current reference max, and its lane sum (no addition of 0 to start)
+      f32x16 pe;
+      float rs;
+      auto exps = [&]() {
+        const float m = m_run[qb];
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) o[qb][db] *= alpha;
-      }
-      const float m = m_run[qb];
-      st[qb][0] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qb][0], c2, -m));
-      float rs = st[qb][0];                               // (no addition of 0 to start)
+        for (int r = 0; r < 16; ++r) pe[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qb][r], c2, -m));
+        rs = pe[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qb][r], c2, -m));
-        st[qb][r] = e;
-        rs += e;
+        for (int r = 1; r < 16; ++r) rs += pe[r];
+      };
+      exps();
+      // Lazy rescale: the reference max moves only when the row max grows by kLazyRescale or
+      // more.  Then the lane holding that max has an exponential above 2^7.8 (while
+      // |m_run| < 2^20, m_run + 8 and max * c2 each round within 2^-4 and the fma once), so
+      // a wave whose lane sums all stay at or below 2^7 cannot need the rescale and skips the
+      // row max; where the rule is checked the values are those of taking the max first, and
+      // a moved reference forms P again.  (The first step, against -inf, sums to +inf.  Past
+      // 2^20 a missed check leaves every value of P below 2^7: the reference lags, still exact.)
+      if (__builtin_amdgcn_ballot_w64(rs > kLazyCheck) != 0) {
+        const float mx = half_pair_max(max16(st[qb])) * c2;  // row max in the log2 domain
+        if (__builtin_amdgcn_ballot_w64(mx > m_run[qb] + kLazyRescale) != 0) {
+          const float m_new = fmaxf(m_run[qb], mx);
+          float dm = m_run[qb] - m_new;
+          // keep the rescale factor's exponential inside the branch: left alone, the compiler
+          // computes it on every step, one quarter-rate instruction per step for nothing
+          asm volatile("" : "+v"(dm));
+          const float alpha = __builtin_amdgcn_exp2f(dm);
+          l_run[qb] *= alpha;
+          m_run[qb] = m_new;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) o[qb][db] *= alpha;
+          exps();
+        }
       }
+      st[qb] = pe;
       l_run[qb] += rs;                                    // lane partial; halves summed at the end
     }
 #pragma unroll

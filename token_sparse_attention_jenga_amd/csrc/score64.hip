@@ -28,6 +28,7 @@
 namespace jenga {
 
 constexpr float kScoreLazy = 8.f;
+constexpr float kScoreCheck = 128.f;   // 2^7: see the lazy rule in k_slse64
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
@@ -98,34 +99,49 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
       for (int r = 0; r < 16; ++r)
         if (kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) > qi) st[r] = -INFINITY;
     }
-    const float mx = half_pair_max(max16(st)) * c2;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kScoreLazy) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      float dm = m_run - m_new;
-      // keep the rescale factor's exponential inside the branch: left alone, the compiler
-      // computes it on every step, one quarter-rate instruction per step for nothing
-      asm volatile("" : "+v"(dm));
-      const float f = __builtin_amdgcn_exp2f(dm);
-      l_run *= (double)f;
-      bsum *= f;
-      m_run = m_new;
-    }
-    if (!diag) {
-      // (the sum starts from its first term: starting from 0 costs an addition per step)
-      float rs = __builtin_amdgcn_exp2f(__builtin_fmaf(st[0], c2, -m_run));
+    // Exponentials against the current reference max, and their sum.  (The sum starts from its
+    // first term: starting from 0 costs an addition per step.)
+    f32x16 ex;
+    float rs;
+    auto exps = [&]() {
 #pragma unroll
-      for (int r = 1; r < 16; ++r) rs += __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c2, -m_run));
-      l_run += (double)rs;
+      for (int r = 0; r < 16; ++r) ex[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c2, -m_run));
+      rs = ex[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) rs += ex[r];
+    };
+    exps();
+    // The lazy rule moves the reference max when some lane's tile max exceeds it by kScoreLazy.
+    // The lane holding that max then has an exponential above 2^7.8 (while |m_run| < 2^20 the
+    // rule's rounded m_run + 8 and max * c2 each lie within 2^-4 of the exact values, and the
+    // fma above rounds once), so its sum exceeds 2^7: a wave whose sums all stay at or below
+    // 2^7 cannot need the rule and skips the tile max.  Where the rule is checked the values
+    // are those of taking the max first; where it moves the reference, the exponentials are
+    // formed again.  (The first step, against m_run = -inf, sums to +inf and always checks.
+    // Past 2^20 a missed check leaves every exponential below 2^7, so the sums stay exact in
+    // range, only their reference differs.)
+    if (__builtin_amdgcn_ballot_w64(rs > kScoreCheck) != 0) {
+      const float mx = half_pair_max(max16(st)) * c2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kScoreLazy) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        float dm = m_run - m_new;
+        // keep the rescale factor's exponential inside the branch: left alone, the compiler
+        // computes it on every step, one quarter-rate instruction per step for nothing
+        asm volatile("" : "+v"(dm));
+        const float f = __builtin_amdgcn_exp2f(dm);
+        l_run *= (double)f;
+        bsum *= f;
+        m_run = m_new;
+        exps();
+      }
+    }
+    l_run += (double)rs;
+    if (!diag) {
       bsum += rs;
     } else {                                             // the mass leaves out the key i = j
-      float rs = 0.f, rm = 0.f;
+      float rm = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c2, -m_run));
-        rs += e;
-        rm += (kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) < qi) ? e : 0.f;
-      }
-      l_run += (double)rs;
+      for (int r = 0; r < 16; ++r) rm += (kr0 + 8 * (r >> 2) + 4 * hl + (r & 3) < qi) ? ex[r] : 0.f;
       bsum += rm;
     }
     if (++in_blk == tpb || diag) {                       // block ends here for these queries
