@@ -671,10 +671,16 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB
   const uint32_t ld_voff = ld_chunk < 8 ? (uint32_t)((const char*)p.wsL2 - (const char*)p.wsD) + 16u * ld_chunk
                                         : 16u * (ld_chunk - 8);
 
-  auto issue = [&](int step, char* buf) {
-    const int hh = step / nq;
-    const int q0 = qstart + (step - hh * nq) * 32;
-    const int h = g * G + hh;
+  // A step's head within the group and query block: the steps run the segment's query blocks
+  // of head g * G, then those of the next head of the group, ...  The loop below walks them one
+  // step at a time (a division per step cost the wave's scalar unit 20 instructions).
+  struct Cur {
+    int hh, qi;
+  };
+  auto next = [&](Cur c) { return ++c.qi == nq ? Cur{c.hh + 1, 0} : c; };
+  auto issue = [&](Cur c, char* buf) {
+    const int q0 = qstart + c.qi * 32;
+    const int h = g * G + c.hh;
     qplan.issue(buf + OFF_Q, rq, (uint32_t)((h * p.qs[2] + (int64_t)kt.pos_u(q0) * p.qs[1]) * 2));
     dplan.issue(buf + OFF_DO, rdo, (uint32_t)(((int64_t)(q0 - qs) * p.Hq + h) * D * 2));
     const uint32_t tile = (uint32_t)((h * (p.seg_len / 32) + (q0 - qs) / 32) * C::TP32);
@@ -684,9 +690,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB
       dma16b(rld, ld_voff, (uint32_t)((h * p.seg_len + (q0 - qs)) * 4), buf + OFF_LD + ld_lds);
   };
 
-  auto compute = [&](int step, const char* buf) {
-    const int hh = step / nq;
-    const int q0 = qstart + (step - hh * nq) * 32;
+  auto compute = [&](Cur c, const char* buf) {
+    const int q0 = qstart + c.qi * 32;
     if (!key_valid || q0 + 31 < kw0) return;
     const char* Ql = buf + OFF_Q;
     const char* dOl = buf + OFF_DO;
@@ -739,17 +744,28 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, char* sA, char* sB
 
   const int s0 = part * nsteps / nparts, s1 = (part + 1) * nsteps / nparts;
   if (s1 > s0) {
-    issue(s0, sA);
+    Cur ci{s0 / nq, s0 % nq};                    // the step issued next
+    Cur cc = ci;                                 // the step computed next
+    issue(ci, sA);
+    ci = next(ci);
     wait_all_mem();
     __syncthreads();
     for (int step = s0; step < s1; step += 2) {
-      if (step + 1 < s1) issue(step + 1, sB);
-      compute(step, sA);
+      if (step + 1 < s1) {
+        issue(ci, sB);
+        ci = next(ci);
+      }
+      compute(cc, sA);
+      cc = next(cc);
       wait_all_mem();
       stage_barrier();
       if (step + 1 >= s1) break;
-      if (step + 2 < s1) issue(step + 2, sA);
-      compute(step + 1, sB);
+      if (step + 2 < s1) {
+        issue(ci, sA);
+        ci = next(ci);
+      }
+      compute(cc, sB);
+      cc = next(cc);
       wait_all_mem();
       stage_barrier();
     }
