@@ -172,6 +172,34 @@ def test_fwd_bwd(J, B, S, Hq, Hkv, D, block, dtype, kept, nseg):
             assert np.all(got[b, elim] == 0), name
 
 
+def test_fwd_bwd_rescale_heavy(J):
+    """Large logits whose scale grows along the sequence: Q times 64 and the keys of token t
+    times 2^(t // 256) (powers of two, exact in bf16), so the logits reach a standard deviation
+    of about 6 in log2 units late in the sequence and most rows move their running maximum
+    many times.  The forward takes the row maximum only where a lane's exponentials sum past
+    2^7, so this exercises its rescale path on most steps.  Gradients scale with Q and K here,
+    so the bf16 bound is taken relative to the largest reference magnitude above 1."""
+    B, S, Hq, Hkv, D, block, nseg = 1, 1024, 4, 2, 128, 64, 3
+    q, k, v, x0, dout = random_inputs(B, S, Hq, Hkv, D, "bf16", seed=77)
+    q = (q * 64.0).astype(np.float32)
+    k = (k * (2.0 ** (np.arange(S) // 256)).astype(np.float32)[None, :, None, None]).astype(np.float32)
+    kept = [[0, 2, 3, 5, 7, 8, 10, 12, 13, 15]]
+    say(f"fwd/bwd rescale-heavy S{S} Hq{Hq} Hkv{Hkv} D{D} block{block} kept={kept} N={nseg}")
+    resid, o_saved, lse, dq, dk, dv = _run_attn(J, q, k, v, x0, dout, kept, block, "bf16", nseg)
+    kept_np = [np.array(x) for x in kept]
+    O, LSE = oracle.attn_fwd(q, k, v, kept_np, block)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, kept_np, block, dout)
+    pos = oracle.token_positions(kept_np[0], block)
+    tol = tol_for("bf16")
+    assert max_abs(o_saved[0, :len(pos)], O[0, pos]) <= tol
+    lr = lse[0][:, :len(pos)]
+    assert np.max(np.abs(lr - LSE[0][:, pos]) / np.maximum(1.0, np.abs(LSE[0][:, pos]))) <= 1e-5
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        scale = max(1.0, float(np.max(np.abs(ref[0, pos]))))
+        err = max_abs(got[0, pos], ref[0, pos])
+        assert err <= tol * scale, (name, err, scale)
+
+
 # Forward over few kept tokens: a row's query tiles of more than 32 key steps run in parts
 # merged by k_fwd_combine.  Row 0 below keeps 40 blocks of 64 (20 tiles of 128 queries: tiles
 # 8..19 split, the last in 3 parts); row 1 keeps 9 blocks (5 tiles, none longer than a part);

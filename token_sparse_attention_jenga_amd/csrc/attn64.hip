@@ -194,9 +194,13 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 3 : 1) void k_fwd64(FwdParams p)
   rp.init();
 
   const rsrc_t rk = make_rsrc(kbase), rv = make_rsrc(vtp);
+  // steps are issued in order s0, s0 + 1, ..., then the last one again (reloads past the end)
+  StepPos sp;
+  sp.init(32 * s0, p.block);
   auto issue = [&](int step, char* buf) {
-    kplan.issue(buf, rk, (uint32_t)(kt.pos_u(step * 32) * kstride));
+    kplan.issue(buf, rk, (uint32_t)(sp.pos(kt) * kstride));
     vplan.issue(buf + OFF_V, rv, (uint32_t)(step * C::TP32));
+    if (step < s0 + nsteps - 1) sp.advance(p.block);
   };
 
   auto compute = [&](int step, const char* buf) {
@@ -900,10 +904,14 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, char* sA, char* sB, 
   tp.init();
 
   const rsrc_t rk = make_rsrc(kbase), rv = make_rsrc(vbase);
+  // steps are issued in order 0, 1, ..., then the last one again (reloads past the end)
+  StepPos sp;
+  sp.init(0, p.block);
   auto issue = [&](int step, char* buf) {
-    const int pos0 = kt.pos_u(step * 32);
+    const int pos0 = sp.pos(kt);
     kplan.issue(buf + OFF_K, rk, (uint32_t)(pos0 * kstride));
     vplan.issue(buf + OFF_V, rv, (uint32_t)(pos0 * vstride));
+    if (step < nsteps - 1) sp.advance(p.block);
   };
 
   auto compute = [&](int step, const char* buf) {

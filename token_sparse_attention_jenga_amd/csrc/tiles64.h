@@ -284,6 +284,35 @@ struct KeptTab {
   }
 };
 
+// pos_u over consecutive 32-rank steps, walked without a division per step: the kept block
+// and the offset in it of the next step's first rank.  Staged loops issue steps in order and
+// call advance() after each step they issue, except past their last one.
+struct StepPos {
+  int kb, off;
+  __device__ void init(int rank, int block) {
+    kb = rank / block;
+    off = rank - kb * block;
+  }
+  __device__ int pos(const KeptTab& kt) const {
+    int v;
+    if (kb < kKeptTab) {
+      v = __builtin_amdgcn_readfirstlane(kt.s[kb]);
+    } else {
+      const int x = kt.g[kb];
+      __builtin_amdgcn_s_waitcnt(0);
+      v = __builtin_amdgcn_readfirstlane(x);
+    }
+    return v * kt.block + off;
+  }
+  __device__ void advance(int block) {
+    off += 32;
+    if (off == block) {
+      off = 0;
+      ++kb;
+    }
+  }
+};
+
 // All threads of the workgroup: copy kept[0..nb) (clipped to the table) into LDS.  The caller
 // synchronises before the first lookup.
 __device__ inline void stage_kept(int* tab, const int32_t* kept, int nb) {
