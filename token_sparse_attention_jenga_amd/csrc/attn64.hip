@@ -101,6 +101,8 @@ constexpr float kLazyCheck = 128.f;    // 2^7: a lane sum above it may need the 
 // SPLIT: the instance for launches where some batch row's long query tiles run in parts (see
 // fwd_row_splits); workgroup x of a (head, batch row) then takes the row's tiles heaviest first
 // and each tile as its parts.  Without it, workgroup x takes tile nqt - 1 - x.
+// Three waves per SIMD, the occupancy the three-buffer ring's LDS allows anyway: the bound keeps
+// the compiler within that occupancy's 168 registers.
 template <int D, int NB, int NW, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, NB == 1 ? 3 : 1) void k_fwd64(FwdParams p) {
   constexpr int RW = 32 * NB, RG = RW * NW;                // rows per wave / per workgroup
