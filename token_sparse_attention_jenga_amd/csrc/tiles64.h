@@ -267,20 +267,19 @@ struct KeptTab {
     const int v = kb < kKeptTab ? s[kb] : g[kb];
     return v * block + (r - kb * block);
   }
-  // The same for a wave-uniform rank, as used by the staged loops.  Each branch ends in a scalar
+  // kept[kb] for a wave-uniform kb, as used by the staged loops.  Each branch ends in a scalar
   // register, and the global branch waits for its own load: were the two joined in one vector
   // register, the common path would wait for every outstanding vector-memory operation.
+  __device__ int entry_u(int kb) const {
+    if (kb < kKeptTab) return __builtin_amdgcn_readfirstlane(s[kb]);
+    const int x = g[kb];
+    __builtin_amdgcn_s_waitcnt(0);
+    return __builtin_amdgcn_readfirstlane(x);
+  }
+  // pos() for a wave-uniform rank
   __device__ int pos_u(int r) const {
     const int kb = r / block;
-    int v;
-    if (kb < kKeptTab) {
-      v = __builtin_amdgcn_readfirstlane(s[kb]);
-    } else {
-      const int x = g[kb];
-      __builtin_amdgcn_s_waitcnt(0);
-      v = __builtin_amdgcn_readfirstlane(x);
-    }
-    return v * block + (r - kb * block);
+    return entry_u(kb) * block + (r - kb * block);
   }
 };
 
@@ -293,17 +292,7 @@ struct StepPos {
     kb = rank / block;
     off = rank - kb * block;
   }
-  __device__ int pos(const KeptTab& kt) const {
-    int v;
-    if (kb < kKeptTab) {
-      v = __builtin_amdgcn_readfirstlane(kt.s[kb]);
-    } else {
-      const int x = kt.g[kb];
-      __builtin_amdgcn_s_waitcnt(0);
-      v = __builtin_amdgcn_readfirstlane(x);
-    }
-    return v * kt.block + off;
-  }
+  __device__ int pos(const KeptTab& kt) const { return kt.entry_u(kb) * kt.block + off; }
   __device__ void advance(int block) {
     off += 32;
     if (off == block) {
