@@ -246,8 +246,10 @@ __global__ __launch_bounds__(64 * NW, NB == 1 ? 3 : 1) void k_fwd64(FwdParams p)
       // |m_run| < 2^20, m_run + 8 and max * c2 each round within 2^-4 and the fma once), so
       // a wave whose lane sums all stay at or below 2^7 cannot need the rescale and skips the
       // row max; where the rule is checked the values are those of taking the max first, and
-      // a moved reference forms P again.  (The first step, against -inf, sums to +inf.  Past
-      // 2^20 a missed check leaves every value of P below 2^7: the reference lags, still exact.)
+      // a moved reference forms P again.  (The first step, against -inf, always checks: a lane
+      // with a masked key sums to NaN there, but the wave's last query sees its whole first
+      // step, so its lanes sum to +inf.  Past 2^20 a missed check leaves every value of P below
+      // 2^7: the reference lags, still exact.)
       if (__builtin_amdgcn_ballot_w64(rs > kLazyCheck) != 0) {
         const float mx = half_pair_max(max16(st[qb])) * c2;  // row max in the log2 domain
         if (__builtin_amdgcn_ballot_w64(mx > m_run[qb] + kLazyRescale) != 0) {

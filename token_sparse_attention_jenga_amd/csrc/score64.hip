@@ -117,9 +117,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_slse64(ScoreParams p) {
     // fma above rounds once), so its sum exceeds 2^7: a wave whose sums all stay at or below
     // 2^7 cannot need the rule and skips the tile max.  Where the rule is checked the values
     // are those of taking the max first; where it moves the reference, the exponentials are
-    // formed again.  (The first step, against m_run = -inf, sums to +inf and always checks.
-    // Past 2^20 a missed check leaves every exponential below 2^7, so the sums stay exact in
-    // range, only their reference differs.)
+    // formed again.  (The first step, against m_run = -inf, always checks: a lane with a masked
+    // key sums to NaN there, but the wave's last query sees the whole first step, so its lanes
+    // sum to +inf.  Past 2^20 a missed check leaves every exponential below 2^7, so the sums stay
+    // exact in range, only their reference differs.)
     if (__builtin_amdgcn_ballot_w64(rs > kScoreCheck) != 0) {
       const float mx = half_pair_max(max16(st)) * c2;
       if (__builtin_amdgcn_ballot_w64(mx > m_run + kScoreLazy) != 0) {
